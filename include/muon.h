@@ -1,0 +1,220 @@
+/*
+ * muon.h -- C ABI of the MI355X (gfx950) Muon optimizer-step library.
+ *
+ * One call of muon_step runs one Muon optimizer step over a group of 2-D
+ * matrices on one GPU, stream-ordered, with no host synchronisation:
+ *
+ *   K1  momentum lerp + Nesterov blend + per-block Frobenius reduction +
+ *       copy into the wide orientation (bf16 or fp32)         (HBM-bound)
+ *   K2  Newton-Schulz, 'standard' or 'gram' form, as grouped MFMA GEMMs
+ *       with the quintic fused into their epilogues            (MFMA-bound)
+ *   K3  transpose back, shape scale, owned-slice scatter into the fp32 flat
+ *       partitions, padding untouched                           (HBM-bound)
+ *
+ * What the step computes comes from the DeepSpeed pull-request pages it is
+ * built from, cited by title and section:
+ *   [8526] "Support Muon in BF16_Optimizer with FP32 gradient accumulation",
+ *          description (fp32 momentum; Muon on the original matrices; only
+ *          each rank's owned intersection is copied into its fp32 partition;
+ *          alignment padding excluded; unsupported set-ups rejected up front).
+ *   [8600] "Run Muon once per optimizer step under ZeRO-3, not once per
+ *          micro-batch", "The problem" / "The change" (once per step on the
+ *          accumulated gradient, after the overflow check and before the
+ *          norm; Newton-Schulz once per matrix per step; full-shape gradients
+ *          passed with each parameter's flat offset) and review thread (the
+ *          per-matrix routine takes momentum, beta, the method 'standard' or
+ *          'gram' and a per-parameter head count).
+ *   [8464] "Fix Muon optimizer under ZeRO CPU offload and bound gather
+ *          buffers", momentum-dtype commit (momentum in the fp32 master
+ *          dtype; padded final partitions).
+ * The numeric form (lerp momentum, Nesterov blend, Frobenius normalisation,
+ * quintic coefficients, wide orientation, shape scale sqrt(max(1,rows/cols)))
+ * is the plain reading of that prose; the library's design notes list every
+ * reading.
+ *
+ * Conventions for every entry point:
+ *  - Every function returns a muon_status; nothing crosses the ABI as an
+ *    exception or abort.  All argument checks run before anything is
+ *    enqueued, so a call that fails has no side effects.  Asynchronous device
+ *    errors surface as MUON_ERR_HIP at a later call or at the caller's own
+ *    synchronisation.  muon_last_error() gives a thread-local detail text.
+ *  - Pointer tables (grads, momenta, partitions, updates, acc, grad_mb) are
+ *    HOST arrays whose elements are DEVICE pointers owned by the caller.
+ *    The library never allocates device memory: the caller supplies every
+ *    buffer and the workspace.
+ *  - Matrices are dense row-major rows x cols in their original orientation.
+ *    Only element alignment is required.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Work is ordered on
+ *    it; no call synchronises the host.  A plan is not thread-safe; distinct
+ *    plans are independent.
+ *  - NaN or Inf inputs are not checked; they propagate to the outputs.
+ */
+#ifndef MUON_MI355X_H
+#define MUON_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MUON_OK = 0,
+  MUON_ERR_INVALID_ARG = 1, /* null pointer, bad size or unknown enum value   */
+  MUON_ERR_UNSUPPORTED = 2, /* a configuration this library does not handle   */
+  MUON_ERR_LAYOUT = 3,      /* flat ranges overlap or exceed the partitions   */
+  MUON_ERR_ALIAS = 4,       /* buffers given to one call overlap              */
+  MUON_ERR_WORKSPACE = 5,   /* workspace missing, too small or misaligned     */
+  MUON_ERR_HIP = 6          /* a HIP runtime call failed                      */
+} muon_status;
+
+typedef enum { MUON_NS_STANDARD = 0, MUON_NS_GRAM = 1 } muon_ns_method;
+
+/* Arithmetic of Newton-Schulz.  FP32: fp32 operands and accumulation
+ * throughout.  BF16: bf16 MFMA operands with fp32 accumulation; the Gram
+ * form's small-side chain (R, P, Q) stays fp32. */
+typedef enum { MUON_PREC_FP32 = 0, MUON_PREC_BF16 = 1 } muon_ns_precision;
+
+/* Storage type of a gradient or update buffer. */
+typedef enum { MUON_DT_FP32 = 0, MUON_DT_BF16 = 1 } muon_dtype;
+
+/* One matrix of the group.  num_heads 0 or 1 = one Newton-Schulz block;
+ * h > 1 = h equal contiguous row blocks, each orthogonalised on its own
+ * ([8600] review thread: the head count is the parameter's own).  flat_offset
+ * = index of element (0,0) in the group's flat index space, which the
+ * partitions cut into num_partitions pieces of partition_numel elements. */
+typedef struct {
+  int64_t rows;
+  int64_t cols;
+  int32_t num_heads;
+  int32_t reserved; /* must be 0 */
+  int64_t flat_offset;
+} muon_matrix;
+
+typedef struct {
+  float beta;          /* momentum coefficient, in [0, 1)                  */
+  int32_t nesterov;    /* 1: u = (1-beta) G + beta m_new;  0: u = m_new    */
+  int32_t method;      /* muon_ns_method                                   */
+  int32_t ns_steps;    /* >= 0                                             */
+  float a, b, c;       /* quintic coefficients, the same at every step     */
+  float eps;           /* X <- u / (||u||_F + eps), per block              */
+  int32_t precision;   /* muon_ns_precision                                */
+  int32_t grad_dtype;  /* muon_dtype of the grads given to muon_step       */
+  uint64_t max_inflight_bytes; /* cap on the workspace; 0 = no cap          */
+} muon_options;
+
+typedef struct {
+  int64_t partition_numel; /* elements per partition (P), > 0          */
+  int32_t num_partitions;  /* R, > 0                                   */
+  int32_t reserved;        /* must be 0                                */
+} muon_layout;
+
+typedef struct {
+  uint64_t steps;          /* muon_step calls that enqueued work          */
+  uint64_t ns_invocations; /* Newton-Schulz runs: one per matrix per step */
+  uint64_t accumulations;  /* muon_accumulate calls that enqueued work    */
+  uint64_t waves;          /* workspace waves per step (>= 1)             */
+} muon_stats;
+
+/* A contiguous owned intersection of one matrix with one partition:
+ * elements [first, first+length) of the row-major flattened matrix go to
+ * partitions[partition][offset .. offset+length). */
+typedef struct {
+  int32_t matrix;
+  int32_t partition;
+  int64_t offset;
+  int64_t first;
+  int64_t length;
+} muon_run;
+
+/* One Newton-Schulz problem of a plan (a whole matrix or one head block),
+ * in its wide orientation m <= n. */
+typedef struct {
+  int32_t matrix;
+  int32_t head;
+  int32_t m, n;
+  int32_t transposed; /* 1 if the block has more rows than columns */
+  int32_t wave;
+  double flops;       /* nominal Newton-Schulz flops of this problem */
+} muon_problem_info;
+
+typedef struct muon_plan muon_plan;
+
+/* Default options: beta 0.95, Nesterov on, standard form, 5 steps,
+ * (a,b,c) = (3.4445, -4.7750, 2.0315), eps 1e-7, bf16 precision, bf16
+ * grads, no workspace cap.  Errors: INVALID_ARG if out is NULL. */
+muon_status muon_default_options(muon_options *out);
+
+/* Build a plan for a group of n matrices (host only; no device call).
+ * The layout is static and computed once ([8526] review thread: split
+ * tables computed at init).  Rejected: n < 1; rows or cols < 1; rows or cols
+ * beyond 2^31-1; num_heads < 0 or not dividing rows; ns_steps < 0; beta
+ * outside [0,1); unknown enums; reserved != 0 (INVALID_ARG / UNSUPPORTED);
+ * flat ranges that overlap or leave [0, R*P) (LAYOUT).  On success *out owns
+ * host memory only, released by muon_plan_destroy. */
+muon_status muon_plan_create(muon_plan **out, const muon_matrix *mats, int32_t n,
+                             const muon_options *opt, const muon_layout *layout);
+
+/* Device workspace muon_step needs, in bytes (256-byte aligned base). */
+muon_status muon_plan_workspace_bytes(const muon_plan *p, size_t *bytes);
+
+/* Gradient accumulation into fp32 ([8526] description; [8600] "The change":
+ * the partitions accumulate the raw gradient, Muon runs only at the step).
+ * acc[i] (fp32, rows x cols) = grad_mb[i] if first != 0, else
+ * acc[i] + grad_mb[i].  mb_dtype: muon_dtype of grad_mb.  Runs no
+ * Newton-Schulz and touches no momentum.  ws/ws_bytes: the plan's workspace
+ * (it holds the launch table).  Errors: INVALID_ARG (null tables or
+ * entries, unknown dtype), ALIAS (any two buffers of the call overlap),
+ * WORKSPACE, HIP. */
+muon_status muon_accumulate(muon_plan *p, float *const *acc, const void *const *grad_mb,
+                            int32_t mb_dtype, int32_t first, void *ws, size_t ws_bytes,
+                            void *stream);
+
+/* One Muon step over the whole group ([8600] "The change": once per
+ * optimizer step, on the accumulated gradient; call it only for steps the
+ * overflow check keeps, so a discarded step leaves momentum untouched).
+ *   grads[i]      read only, rows x cols, opt.grad_dtype
+ *   momenta[i]    fp32 rows x cols, updated in place
+ *   partitions[r] fp32, partition_numel each; written only on the owned
+ *                 intersections of the matrices, never on padding
+ *   ws, ws_bytes  device workspace of at least muon_plan_workspace_bytes,
+ *                 256-byte aligned; its contents need not be preserved
+ *                 between calls
+ * Errors: INVALID_ARG (null table or entry), ALIAS (any two buffers of the
+ * call overlap, the workspace included), WORKSPACE (too small / unaligned),
+ * HIP (a launch failed). */
+muon_status muon_step(muon_plan *p, const void *const *grads, float *const *momenta,
+                      float *const *partitions, void *ws, size_t ws_bytes, void *stream);
+
+/* The writeback alone (the same kernel muon_step ends with): for every
+ * matrix i, partitions[r][...] = fp32(updates[i][j]) * fp32(sqrt(max(1,
+ * rows/cols))) on the owned intersections, one IEEE round-to-nearest
+ * multiply, padding untouched.  updates[i] is the unscaled Newton-Schulz
+ * output in the original orientation, dense rows x cols of dtype `dtype`.
+ * ws/ws_bytes: the plan's workspace (it holds the run table).
+ * Errors: INVALID_ARG, ALIAS, WORKSPACE, HIP. */
+muon_status muon_scatter(muon_plan *p, const void *const *updates, int32_t dtype,
+                         float *const *partitions, void *ws, size_t ws_bytes, void *stream);
+
+/* Counters of the plan ([8600] results table counts Newton-Schulz calls). */
+muon_status muon_plan_stats(const muon_plan *p, muon_stats *out);
+
+/* Host-side introspection of the static layout (no device call).
+ * muon_plan_runs: the owned intersections of matrix `matrix`, in element
+ * order; writes min(cap, total) runs and sets *count to the total.
+ * muon_plan_problems: the Newton-Schulz problems in plan order, likewise. */
+muon_status muon_plan_runs(const muon_plan *p, int32_t matrix, muon_run *out, int32_t cap,
+                           int32_t *count);
+muon_status muon_plan_problems(const muon_plan *p, muon_problem_info *out, int32_t cap,
+                               int32_t *count);
+
+void muon_plan_destroy(muon_plan *p);
+const char *muon_status_string(muon_status s);
+const char *muon_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_MI355X_H */

@@ -1,0 +1,98 @@
+"""Muon optimizer step on MI355X (gfx950): momentum, Newton-Schulz and the
+flat-partition writeback as HIP kernels behind a C ABI (include/muon.h).
+
+This package is the Python face of that library: ``_lib`` binds the C entry
+points by name; ``MuonGroup`` is a small convenience wrapper that owns a plan.
+Device memory and streams come from the caller (e.g. torch tensors).
+"""
+
+from __future__ import annotations
+
+from . import _lib
+from ._lib import (DTYPE, EXPORTS, NS_METHOD, PRECISION, MuonError, load, muon_accumulate,  # noqa: F401
+                   muon_default_options, muon_last_error, muon_layout, muon_plan_create, muon_plan_destroy,
+                   muon_plan_problems, muon_plan_runs, muon_plan_stats, muon_plan_workspace_bytes, muon_scatter,
+                   muon_status_string, muon_step)
+
+__all__ = ["MuonGroup", "pack_layout", "MuonError", "load"] + list(EXPORTS)
+
+
+def pack_layout(shapes, num_partitions: int, align: int = 16, interior_align: bool = False):
+    """Flat layout of a group: matrices back to back in order (each start
+    rounded up to `align` if interior_align), the total padded at the tail so
+    the partition size is a multiple of `align`.  Returns (offsets, P)."""
+    offsets, f = [], 0
+    for r, c in shapes:
+        if interior_align:
+            f = -(-f // align) * align
+        offsets.append(f)
+        f += int(r) * int(c)
+    per = -(-f // (num_partitions * align)) * align
+    return offsets, max(per, align)
+
+
+class MuonGroup:
+    """A plan over one group of matrices (host memory only until used)."""
+
+    def __init__(self, shapes, heads=None, offsets=None, num_partitions: int = 1, partition_numel=None,
+                 align: int = 16, method: str = "standard", precision: str = "bf16", grad_dtype: str = "bf16",
+                 ns_steps: int = 5, beta: float = 0.95, nesterov: bool = True, coeffs=None, eps=None,
+                 max_inflight_bytes: int = 0):
+        self.shapes = [(int(r), int(c)) for r, c in shapes]
+        self.heads = list(heads) if heads is not None else [0] * len(self.shapes)
+        if offsets is None or partition_numel is None:
+            offs, P = pack_layout(self.shapes, num_partitions, align)
+            offsets = offsets if offsets is not None else offs
+            partition_numel = partition_numel if partition_numel is not None else P
+        self.offsets = [int(o) for o in offsets]
+        self.num_partitions = int(num_partitions)
+        self.partition_numel = int(partition_numel)
+        self.grad_dtype = grad_dtype
+        self.precision = precision
+        self.method = method
+        o = muon_default_options()
+        o.beta = beta
+        o.nesterov = int(bool(nesterov))
+        o.method = NS_METHOD[method]
+        o.ns_steps = int(ns_steps)
+        if coeffs is not None:
+            o.a, o.b, o.c = coeffs
+        if eps is not None:
+            o.eps = eps
+        o.precision = PRECISION[precision]
+        o.grad_dtype = DTYPE[grad_dtype]
+        o.max_inflight_bytes = int(max_inflight_bytes)
+        self.options = o
+        lay = muon_layout(self.partition_numel, self.num_partitions, 0)
+        mats = [(r, c, h, off) for (r, c), h, off in zip(self.shapes, self.heads, self.offsets)]
+        self.plan = muon_plan_create(mats, o, lay)
+        self.workspace_bytes = muon_plan_workspace_bytes(self.plan)
+
+    def step(self, grads, momenta, partitions, ws, stream=None):
+        muon_step(self.plan, grads, momenta, partitions, ws, self.workspace_bytes, stream)
+
+    def accumulate(self, acc, grad_mb, mb_dtype: str, first: bool, ws, stream=None):
+        muon_accumulate(self.plan, acc, grad_mb, mb_dtype, first, ws, self.workspace_bytes, stream)
+
+    def scatter(self, updates, dtype: str, partitions, ws, stream=None):
+        muon_scatter(self.plan, updates, dtype, partitions, ws, self.workspace_bytes, stream)
+
+    def stats(self) -> dict:
+        return muon_plan_stats(self.plan)
+
+    def runs(self, matrix: int) -> list:
+        return muon_plan_runs(self.plan, matrix)
+
+    def problems(self) -> list:
+        return muon_plan_problems(self.plan)
+
+    def close(self):
+        if getattr(self, "plan", None):
+            muon_plan_destroy(self.plan)
+            self.plan = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

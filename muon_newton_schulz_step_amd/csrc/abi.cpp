@@ -1,0 +1,292 @@
+// C ABI entry points that touch the device: muon_step, muon_accumulate,
+// muon_scatter, muon_plan_destroy.  All argument checks run before anything
+// is enqueued.  Launch tables are uploaded into the head of the caller's
+// workspace from pinned host staging (two slots, each guarded by an event,
+// so the host never overwrites a buffer the copy engine still reads).
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstddef>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "elem.hpp"
+#include "muon.h"
+#include "plan.hpp"
+
+using namespace muon;
+
+namespace {
+
+struct Range {
+  uintptr_t lo, hi;
+  const char *what;
+  int64_t index;
+};
+
+muon_status check_alias(std::vector<Range> &rs) {
+  std::sort(rs.begin(), rs.end(), [](const Range &a, const Range &b) { return a.lo < b.lo; });
+  for (size_t i = 1; i < rs.size(); ++i) {
+    if (rs[i].lo < rs[i - 1].hi) {
+      set_error(std::string("buffers overlap: ") + rs[i - 1].what + "[" + std::to_string(rs[i - 1].index) + "] and " +
+                rs[i].what + "[" + std::to_string(rs[i].index) + "]");
+      return MUON_ERR_ALIAS;
+    }
+  }
+  return MUON_OK;
+}
+
+muon_status hip_fail(hipError_t e, const char *where) {
+  set_error(std::string(where) + ": " + hipGetErrorString(e));
+  return MUON_ERR_HIP;
+}
+
+muon_status ensure_staging(muon_plan *p, size_t bytes) {
+  if (p->staging_bytes >= bytes && p->staging[0]) return MUON_OK;
+  for (int s = 0; s < 2; ++s) {
+    if (p->event_live[s]) {
+      hipError_t e = hipEventSynchronize((hipEvent_t)p->events[s]);
+      if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+      p->event_live[s] = false;
+    }
+    if (p->staging[s]) {
+      (void)hipHostFree(p->staging[s]);
+      p->staging[s] = nullptr;
+    }
+  }
+  p->staging_bytes = 0;
+  const size_t want = std::max<size_t>(bytes, 4096);
+  for (int s = 0; s < 2; ++s) {
+    hipError_t e = hipHostMalloc(&p->staging[s], want, hipHostMallocDefault);
+    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc (table staging)");
+    if (!p->events[s]) {
+      hipEvent_t ev;
+      e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+      if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+      p->events[s] = ev;
+    }
+  }
+  p->staging_bytes = want;
+  return MUON_OK;
+}
+
+// Take the next staging slot once the copy that last used it has finished.
+muon_status acquire_slot(muon_plan *p, size_t bytes, char **host, int *slot) {
+  muon_status st = ensure_staging(p, bytes);
+  if (st != MUON_OK) return st;
+  const int s = p->slot;
+  p->slot ^= 1;
+  if (p->event_live[s]) {
+    hipError_t e = hipEventSynchronize((hipEvent_t)p->events[s]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    p->event_live[s] = false;
+  }
+  *host = static_cast<char *>(p->staging[s]);
+  *slot = s;
+  return MUON_OK;
+}
+
+muon_status upload(muon_plan *p, int slot, void *dst, size_t bytes, hipStream_t s) {
+  if (bytes == 0) return MUON_OK;
+  hipError_t e = hipMemcpyAsync(dst, p->staging[slot], bytes, hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (tables)");
+  e = hipEventRecord((hipEvent_t)p->events[slot], s);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  p->event_live[slot] = true;
+  return MUON_OK;
+}
+
+size_t dtype_size(int32_t dt) { return dt == MUON_DT_BF16 ? 2 : 4; }
+
+muon_status check_ws(const muon_plan *p, void *ws, size_t ws_bytes, size_t need) {
+  if (!ws) { set_error("workspace is NULL"); return MUON_ERR_WORKSPACE; }
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) { set_error("workspace must be 256-byte aligned"); return MUON_ERR_WORKSPACE; }
+  if (ws_bytes < need) {
+    set_error("workspace too small: " + std::to_string(ws_bytes) + " < " + std::to_string(need));
+    return MUON_ERR_WORKSPACE;
+  }
+  (void)p;
+  return MUON_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+muon_status muon_step(muon_plan *p, const void *const *grads, float *const *momenta, float *const *partitions, void *ws,
+                      size_t ws_bytes, void *stream) {
+  if (!p || !grads || !momenta || !partitions) { set_error("muon_step: NULL argument"); return MUON_ERR_INVALID_ARG; }
+  const int32_t nmat = (int32_t)p->mats.size();
+  const int32_t R = p->layout.num_partitions;
+  const size_t gsz = dtype_size(p->opt.grad_dtype);
+  std::vector<Range> rs;
+  rs.reserve(2 * nmat + R + 1);
+  for (int32_t i = 0; i < nmat; ++i) {
+    if (!grads[i] || !momenta[i]) { set_error("muon_step: NULL grads/momenta entry " + std::to_string(i)); return MUON_ERR_INVALID_ARG; }
+    const uintptr_t n = (uintptr_t)(p->mats[i].desc.rows * p->mats[i].desc.cols);
+    rs.push_back({(uintptr_t)grads[i], (uintptr_t)grads[i] + n * gsz, "grads", i});
+    rs.push_back({(uintptr_t)momenta[i], (uintptr_t)momenta[i] + n * 4, "momenta", i});
+  }
+  for (int32_t r = 0; r < R; ++r) {
+    if (!partitions[r]) { set_error("muon_step: NULL partition " + std::to_string(r)); return MUON_ERR_INVALID_ARG; }
+    rs.push_back({(uintptr_t)partitions[r], (uintptr_t)partitions[r] + (uintptr_t)p->layout.partition_numel * 4,
+                  "partitions", r});
+  }
+  muon_status st = check_ws(p, ws, ws_bytes, (size_t)p->ws_bytes);
+  if (st != MUON_OK) return st;
+  rs.push_back({(uintptr_t)ws, (uintptr_t)ws + ws_bytes, "workspace", 0});
+  if ((st = check_alias(rs)) != MUON_OK) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char *h = nullptr;
+  int slot = 0;
+  if ((st = acquire_slot(p, p->host_tables.size(), &h, &slot)) != MUON_OK) return st;
+  std::memcpy(h, p->host_tables.data(), p->host_tables.size());
+  char *wsb = static_cast<char *>(ws);
+  for (const WavePlan &W : p->waves) {
+    K1Prob *k1 = reinterpret_cast<K1Prob *>(h + W.off_k1);
+    for (size_t j = 0; j < W.k1.size(); ++j) {
+      k1[j].grad = grads[W.k1_matrix[j]];
+      k1[j].mom = momenta[W.k1_matrix[j]];
+    }
+    K3Run *runs = reinterpret_cast<K3Run *>(h + W.off_runs);
+    for (size_t j = 0; j < W.runs.size(); ++j) {
+      const muon_run &r = W.run_src[j];
+      runs[j].src = wsb + p->mats[r.matrix].u_off;
+      runs[j].dst = partitions[r.partition] + r.offset;
+    }
+  }
+  if ((st = upload(p, slot, ws, p->host_tables.size(), s)) != MUON_OK) return st;
+
+  const bool gbf16 = p->opt.grad_dtype == MUON_DT_BF16;
+  float *partials = reinterpret_cast<float *>(wsb + p->partials_off);
+  float *scales = reinterpret_cast<float *>(wsb + p->scales_off);
+  hipError_t e;
+  for (const WavePlan &W : p->waves) {
+    const int np = (int)W.probs.size();
+    const K1Prob *k1 = reinterpret_cast<const K1Prob *>(wsb + W.off_k1);
+    const ProbDev *probs = reinterpret_cast<const ProbDev *>(wsb + W.off_prob);
+    const K3Run *runs = reinterpret_cast<const K3Run *>(wsb + W.off_runs);
+    if ((e = launch_k1(k1, np, W.k1_tiles, wsb, partials, p->opt.beta, p->opt.nesterov, gbf16, s)) != hipSuccess)
+      return hip_fail(e, "K1 launch");
+    if ((e = launch_kn(k1, np, partials, scales, p->opt.eps, s)) != hipSuccess) return hip_fail(e, "norm launch");
+    if (p->opt.ns_steps == 0) {
+      if ((e = launch_kc(probs, k1, np, wsb, scales, s)) != hipSuccess) return hip_fail(e, "copy launch");
+    } else {
+      // bf16-operand problems first (the bulk of the work), then fp32-operand ones
+      for (int cls = 1; cls >= 0; --cls) {
+        const int nmm = (int)W.tiles_mm[cls].size(), nmn = (int)W.tiles_mn[cls].size();
+        if (nmn == 0) continue;
+        const TileDev *tmm = reinterpret_cast<const TileDev *>(wsb + W.off_tiles_mm[cls]);
+        const TileDev *tmn = reinterpret_cast<const TileDev *>(wsb + W.off_tiles_mn[cls]);
+        for (const Launch &L : p->schedule[cls]) {
+          GemmArgs a{probs, L.mn ? tmn : tmm, wsb, scales, L.r};
+          if ((e = launch_gemm(L.kind == Launch::GEMM_OP, a, L.mn ? nmn : nmm, s)) != hipSuccess)
+            return hip_fail(e, "Newton-Schulz launch");
+        }
+      }
+    }
+    if ((e = launch_k3(runs, (int)W.runs.size(), W.k3_chunks, s)) != hipSuccess) return hip_fail(e, "K3 launch");
+  }
+  p->stats.steps += 1;
+  p->stats.ns_invocations += (uint64_t)nmat;
+  return MUON_OK;
+}
+
+muon_status muon_accumulate(muon_plan *p, float *const *acc, const void *const *grad_mb, int32_t mb_dtype,
+                            int32_t first, void *ws, size_t ws_bytes, void *stream) {
+  if (!p || !acc || !grad_mb) { set_error("muon_accumulate: NULL argument"); return MUON_ERR_INVALID_ARG; }
+  if (mb_dtype != MUON_DT_FP32 && mb_dtype != MUON_DT_BF16) { set_error("muon_accumulate: unknown dtype"); return MUON_ERR_INVALID_ARG; }
+  const int32_t nmat = (int32_t)p->mats.size();
+  const size_t gsz = dtype_size(mb_dtype);
+  std::vector<Range> rs;
+  std::vector<K0Mat> tab(nmat);
+  int64_t ch = 0;
+  for (int32_t i = 0; i < nmat; ++i) {
+    if (!acc[i] || !grad_mb[i]) { set_error("muon_accumulate: NULL entry " + std::to_string(i)); return MUON_ERR_INVALID_ARG; }
+    const int64_t n = p->mats[i].desc.rows * p->mats[i].desc.cols;
+    rs.push_back({(uintptr_t)acc[i], (uintptr_t)acc[i] + (uintptr_t)n * 4, "acc", i});
+    rs.push_back({(uintptr_t)grad_mb[i], (uintptr_t)grad_mb[i] + (uintptr_t)n * gsz, "grad_mb", i});
+    tab[i] = K0Mat{acc[i], grad_mb[i], n, ch};
+    ch += (n + K0_CHUNK - 1) / K0_CHUNK;
+  }
+  const size_t tb = tab.size() * sizeof(K0Mat);
+  muon_status st = check_ws(p, ws, ws_bytes, tb);
+  if (st != MUON_OK) return st;
+  rs.push_back({(uintptr_t)ws, (uintptr_t)ws + ws_bytes, "workspace", 0});
+  if ((st = check_alias(rs)) != MUON_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char *h = nullptr;
+  int slot = 0;
+  if ((st = acquire_slot(p, std::max<size_t>(tb, p->host_tables.size()), &h, &slot)) != MUON_OK) return st;
+  std::memcpy(h, tab.data(), tb);
+  if ((st = upload(p, slot, ws, tb, s)) != MUON_OK) return st;
+  hipError_t e = launch_k0(static_cast<const K0Mat *>(ws), nmat, ch, mb_dtype == MUON_DT_BF16, first ? 1 : 0, s);
+  if (e != hipSuccess) return hip_fail(e, "accumulate launch");
+  p->stats.accumulations += 1;
+  return MUON_OK;
+}
+
+muon_status muon_scatter(muon_plan *p, const void *const *updates, int32_t dtype, float *const *partitions, void *ws,
+                         size_t ws_bytes, void *stream) {
+  if (!p || !updates || !partitions) { set_error("muon_scatter: NULL argument"); return MUON_ERR_INVALID_ARG; }
+  if (dtype != MUON_DT_FP32 && dtype != MUON_DT_BF16) { set_error("muon_scatter: unknown dtype"); return MUON_ERR_INVALID_ARG; }
+  const int32_t nmat = (int32_t)p->mats.size();
+  const int32_t R = p->layout.num_partitions;
+  const size_t usz = dtype_size(dtype);
+  std::vector<Range> rs;
+  for (int32_t i = 0; i < nmat; ++i) {
+    if (!updates[i]) { set_error("muon_scatter: NULL update " + std::to_string(i)); return MUON_ERR_INVALID_ARG; }
+    const int64_t n = p->mats[i].desc.rows * p->mats[i].desc.cols;
+    rs.push_back({(uintptr_t)updates[i], (uintptr_t)updates[i] + (uintptr_t)n * usz, "updates", i});
+  }
+  for (int32_t r = 0; r < R; ++r) {
+    if (!partitions[r]) { set_error("muon_scatter: NULL partition " + std::to_string(r)); return MUON_ERR_INVALID_ARG; }
+    rs.push_back({(uintptr_t)partitions[r], (uintptr_t)partitions[r] + (uintptr_t)p->layout.partition_numel * 4,
+                  "partitions", r});
+  }
+  std::vector<K3Run> tab;
+  int64_t ch = 0;
+  for (int32_t i = 0; i < nmat; ++i) {
+    for (const muon_run &r : p->mats[i].runs) {
+      K3Run k;
+      std::memset(&k, 0, sizeof(k));
+      k.src = updates[i];
+      k.dst = partitions[r.partition] + r.offset;
+      k.first = r.first;
+      k.length = r.length;
+      k.chunk0 = ch;
+      k.scale = p->mats[i].scale;
+      k.src_bf16 = dtype == MUON_DT_BF16 ? 1 : 0;
+      ch += (r.length + K3_CHUNK - 1) / K3_CHUNK;
+      tab.push_back(k);
+    }
+  }
+  const size_t tb = tab.size() * sizeof(K3Run);
+  muon_status st = check_ws(p, ws, ws_bytes, tb);
+  if (st != MUON_OK) return st;
+  rs.push_back({(uintptr_t)ws, (uintptr_t)ws + ws_bytes, "workspace", 0});
+  if ((st = check_alias(rs)) != MUON_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char *h = nullptr;
+  int slot = 0;
+  if ((st = acquire_slot(p, std::max<size_t>(tb, p->host_tables.size()), &h, &slot)) != MUON_OK) return st;
+  std::memcpy(h, tab.data(), tb);
+  if ((st = upload(p, slot, ws, tb, s)) != MUON_OK) return st;
+  hipError_t e = launch_k3(static_cast<const K3Run *>(ws), (int)tab.size(), ch, s);
+  if (e != hipSuccess) return hip_fail(e, "scatter launch");
+  return MUON_OK;
+}
+
+void muon_plan_destroy(muon_plan *p) {
+  if (!p) return;
+  for (int s = 0; s < 2; ++s) {
+    if (p->event_live[s]) (void)hipEventSynchronize((hipEvent_t)p->events[s]);
+    if (p->staging[s]) (void)hipHostFree(p->staging[s]);
+    if (p->events[s]) (void)hipEventDestroy((hipEvent_t)p->events[s]);
+  }
+  delete p;
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// Host planner of the Muon step: validation, orientation, head blocks, owned
+// runs, workspace carving, LPT-ordered tile lists and launch recipes.  Host
+// code only; it makes no HIP call, so it is testable without a GPU.
+#pragma once
+
+#include <string>
+#include <vector>
+
+#include "muon.h"
+#include "tables.hpp"
+
+namespace muon {
+
+void set_error(const std::string &msg);
+const char *last_error();
+
+struct MatrixPlan {
+  muon_matrix desc;
+  int32_t heads;     // >= 1
+  int64_t hr;        // rows per head block
+  int32_t prob0;     // first problem (global index)
+  int32_t wave;
+  float scale;       // fp32 shape scale sqrt(max(1, rows/cols))
+  std::vector<muon_run> runs;
+  bool ops32;                    // Newton-Schulz operands fp32 (else bf16)
+  int64_t elem;                  // operand element bytes (4 or 2)
+  int64_t ldc, ldhr;             // padded leading dims of the two copies
+  int64_t orig_off[2];           // relative to the data base of the wave
+  int64_t trans_off[2];          // -1 if not allocated
+  int64_t u_off;                 // absolute workspace offset of the dense output
+};
+
+struct ProblemPlan {
+  int32_t matrix, head;
+  int32_t m, n;
+  bool tall;
+  double flops;
+  int64_t ldm;
+  int64_t mm_off[6];  // R_MA .. R_QB relative to the data base; -1 unused
+};
+
+struct WavePlan {
+  std::vector<int32_t> matrices;
+  std::vector<int32_t> problems;  // global ids in LPT order (wave-local index = position)
+  int64_t data_bytes = 0;
+  // byte offsets of this wave's tables inside the workspace
+  // tile lists per operand class: [0] fp32 operands, [1] bf16 operands
+  int64_t off_prob = 0, off_k1 = 0, off_tiles_mm[2] = {0, 0}, off_tiles_mn[2] = {0, 0}, off_runs = 0;
+  std::vector<ProbDev> probs;
+  std::vector<K1Prob> k1;
+  std::vector<TileDev> tiles_mm[2], tiles_mn[2];
+  std::vector<K3Run> runs;
+  std::vector<muon_run> run_src;     // the owned run behind each K3 entry (to patch pointers)
+  std::vector<int32_t> k1_matrix;    // matrix of each K1 problem
+  int32_t k1_tiles = 0;
+  int64_t k3_chunks = 0;
+};
+
+// Step of the launch schedule.
+struct Launch {
+  enum Kind { GEMM_OP, GEMM_F32, COPY_SCALED } kind;
+  GemmRecipe r;
+  bool mn;  // tile list: false = m x m (symmetric), true = m x n
+};
+
+}  // namespace muon
+
+struct muon_plan {
+  muon_options opt;
+  muon_layout layout;
+  std::vector<muon::MatrixPlan> mats;
+  std::vector<muon::ProblemPlan> probs;
+  std::vector<muon::WavePlan> waves;
+  std::vector<muon::Launch> schedule[2];  // per operand class: [0] fp32, [1] bf16
+  int64_t tables_bytes = 0;  // all waves' tables, at the head of the workspace
+  int64_t partials_off = 0, scales_off = 0, data_off = 0, ws_bytes = 0;
+  int64_t max_k1_tiles = 0, max_probs = 0;
+  int64_t k0_table_bytes = 0;  // accumulation table (shares the table region)
+  std::vector<char> host_tables;  // serialized tables (pointers patched per call)
+  // lazily created HIP resources (pinned staging, events), see abi.cpp
+  void *staging[2] = {nullptr, nullptr};
+  size_t staging_bytes = 0;
+  void *events[2] = {nullptr, nullptr};
+  bool event_live[2] = {false, false};
+  int slot = 0;
+  muon_stats stats{};
+};
+
+namespace muon {
+muon_status build_plan(muon_plan *p);
+}

@@ -1,0 +1,70 @@
+"""Helpers of the GPU tests: move seeded inputs to the device, run the HIP
+path through the C ABI, read results back."""
+
+from __future__ import annotations
+
+import numpy as np
+
+SENTINEL = 0x7FBADBAD
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def to_device(arr: np.ndarray, dtype: str):
+    torch = torch_mod()
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    return t.to("cuda:0")
+
+
+def sentinel_partitions(R: int, P: int):
+    torch = torch_mod()
+    bits = np.full(P, SENTINEL, dtype=np.uint32).view(np.int32)
+    return [torch.from_numpy(bits.copy()).to("cuda:0").view(torch.float32) for _ in range(R)]
+
+
+def workspace(nbytes: int):
+    torch = torch_mod()
+    ws = torch.empty(max(nbytes, 256) + 256, dtype=torch.uint8, device="cuda:0")
+    off = (-ws.data_ptr()) % 256
+    return ws, ws.data_ptr() + off
+
+
+def host(t) -> np.ndarray:
+    torch = torch_mod()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.detach().cpu().numpy()
+
+
+def run_steps(group, micro_grads, micro_dtype: str, momenta0=None, use_accumulate=True):
+    """micro_grads[step][micro][matrix] host arrays (storage form).  Returns
+    (partitions as float32 arrays, momenta as float32 arrays)."""
+    torch = torch_mod()
+    shapes = group.shapes
+    ws_t, ws = workspace(group.workspace_bytes)
+    if momenta0 is None:
+        moms = [torch.zeros(r, c, dtype=torch.float32, device="cuda:0") for r, c in shapes]
+    else:
+        moms = [to_device(m, "fp32").reshape(r, c) for m, (r, c) in zip(momenta0, shapes)]
+    parts = sentinel_partitions(group.num_partitions, group.partition_numel)
+    accs = [torch.empty(r, c, dtype=torch.float32, device="cuda:0") for r, c in shapes]
+    for step in micro_grads:
+        if use_accumulate:
+            for k, mb in enumerate(step):
+                dev = [to_device(g, micro_dtype) for g in mb]
+                group.accumulate(accs, dev, micro_dtype, k == 0, ws)
+                torch.cuda.synchronize()
+            group.step(accs, moms, parts, ws)
+        else:
+            assert len(step) == 1
+            dev = [to_device(g, micro_dtype) for g in step[0]]
+            group.step(dev, moms, parts, ws)
+        torch.cuda.synchronize()
+    del ws_t
+    return [host(p) for p in parts], [host(m) for m in moms]
