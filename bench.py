@@ -1,0 +1,280 @@
+#!/usr/bin/env python
+"""Benchmark of the Muon group step on one MI355X.
+
+A step here is one pass of the whole hot path over one batch of synthetic
+input: fp32 accumulation of the workload's micro-batch gradients, then
+muon_step (K1 momentum/norm/copies, grouped Newton-Schulz, K3 scatter).
+`value` is the group-step time (muon_step alone, HIP events on the library's
+stream, mean over the timed steps); the accumulation is timed beside it.
+Inputs are generated on the GPU before the timed region (seeded, Gaussian,
+the workload's shapes and sigma).
+
+    python bench.py [--steps K] [--warmup W] [--workload llama7b_32layer]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "Muon group-step time (ms) + NS TFLOP/s as % of bf16 MFMA peak, Llama-7B shapes"
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def ns_flops(problems, method: str, steps: int):
+    """(nominal, symmetric) Newton-Schulz flops of a group.
+
+    nominal: every product counted in full (standard 20 m^2 n + 10 m^3,
+    Gram 4 m^2 n + 34 m^3 at 5 steps).  symmetric: products whose result is
+    symmetric (X X^T, A A, and the Gram chain) counted once per output pair,
+    which is what the grouped kernel executes (upper-triangle tiles only)."""
+    nom = sym = 0.0
+    for q in problems:
+        m, n = float(q["m"]), float(q["n"])
+        if steps == 0:
+            continue
+        if method == "standard":
+            nom += steps * (4 * m * m * n + 2 * m ** 3)
+            sym += steps * (3 * m * m * n + m ** 3)
+        else:
+            chain = steps + (steps - 1) + 2 * (steps - 1)
+            nom += 4 * m * m * n + chain * 2 * m ** 3
+            sym += 3 * m * m * n + chain * m ** 3
+    return nom, sym
+
+
+def make_inputs(torch, wl, seed: int):
+    """Flat device buffers with per-matrix views: micro-batch gradients (two
+    buffers, alternated over the micro-batches), the fp32 accumulator (if
+    gas > 1), momentum and partitions."""
+    dev = torch.device("cuda:0")
+    total = wl.numel
+    mdt = torch.bfloat16 if wl.micro_dtype == "bf16" else torch.float32
+    nbuf = min(wl.gas, 2)
+    gen = torch.Generator(device=dev)
+    mbs = []
+    for b in range(nbuf):
+        flat = torch.empty(total, dtype=mdt, device=dev)
+        gen.manual_seed(seed + 7919 * b)
+        off = 0
+        views = []
+        for (r, c) in wl.shapes:
+            v = flat[off:off + r * c].view(r, c)
+            v.copy_(torch.randn((r, c), generator=gen, device=dev, dtype=torch.float32).mul_(wl.sigma))
+            views.append(v)
+            off += r * c
+        mbs.append((flat, views))
+    acc = None
+    if wl.gas > 1:
+        flat = torch.empty(total, dtype=torch.float32, device=dev)
+        acc = (flat, _views(flat, wl.shapes))
+    mom = torch.zeros(total, dtype=torch.float32, device=dev)
+    return mbs, acc, (mom, _views(mom, wl.shapes))
+
+
+def _views(flat, shapes):
+    out, off = [], 0
+    for (r, c) in shapes:
+        out.append(flat[off:off + r * c].view(r, c))
+        off += r * c
+    return out
+
+
+def cpu_baseline(wl, method: str, total_nominal: float, budget_s: float):
+    """The oracle (fp64 numpy, as it stands) on a bounded sample: the first
+    matrix of the group run through the whole step (momentum, Newton-Schulz,
+    shape scale, writeback), extrapolated to the group by nominal
+    Newton-Schulz flops."""
+    import numpy as np
+    import oracle.muon_oracle as O
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info() if t.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    # pick the largest matrix kind whose estimated fp64 time fits the budget
+    shapes = sorted(set(wl.shapes), key=lambda s: s[0] * s[1])
+    probe = O.ns_standard(W.gaussian((512, 512), 1, 1.0).astype(np.float64) / 512.0)  # warm the BLAS
+    del probe
+    t0 = time.perf_counter()
+    x = W.gaussian((1024, 1024), 2, 1.0).astype(np.float64)
+    _ = x @ x
+    gflops = 2 * 1024 ** 3 / (time.perf_counter() - t0) / 1e9
+    pick = shapes[0]
+    heads = 0
+    for s in shapes:
+        i = wl.shapes.index(s)
+        h = wl.heads[i] or 1
+        m, n = min(s[0] // h, s[1]), max(s[0] // h, s[1])
+        f = h * (5 * (4 * m * m * n + 2 * m ** 3) if method == "standard" else 4 * m * m * n + 34 * m ** 3)
+        if f / (gflops * 1e9) <= budget_s:
+            pick, heads = s, wl.heads[i]
+    r, c = pick
+    h = heads or 1
+    m, n = min(r // h, c), max(r // h, c)
+    sample_flops = h * (5 * (4 * m * m * n + 2 * m ** 3) if method == "standard" else 4 * m * m * n + 34 * m ** 3)
+    g = W.gaussian(pick, 12345, wl.sigma).astype(np.float64)
+    state = O.init_state([pick])
+    offsets, P = O.pack_layout([pick], 1, 16)
+    t0 = time.perf_counter()
+    O.muon_step([g], state, [pick], [heads], offsets, 1, P, O.MuonOptions(method=method))
+    dt = time.perf_counter() - t0
+    ms = dt * 1e3 * total_nominal / sample_flops
+    return {"value": round(ms, 1), "unit": "ms", "cores": int(threads), "kind": "oracle",
+            "sample": (f"one {r}x{c} matrix{' (%d heads)' % heads if heads else ''} through the oracle step "
+                       f"(fp64 numpy) in {dt:.2f} s, extrapolated to the {len(wl.shapes)}-matrix group by "
+                       f"nominal Newton-Schulz flops ({sample_flops / 1e12:.3f} of {total_nominal / 1e12:.1f} TFLOP)"),
+            "extrapolated": True}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="llama7b_32layer")
+    ap.add_argument("--method", default=None)
+    ap.add_argument("--precision", default="bf16")
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import muon_newton_schulz_step_amd as M
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    M.load()
+    wl = W.ALL[args.workload]()
+    method = args.method or wl.methods[0]
+    offsets, P = M.pack_layout(wl.shapes, wl.num_partitions, wl.align)
+    step_dtype = "fp32" if wl.gas > 1 else wl.micro_dtype
+    g = M.MuonGroup(wl.shapes, heads=wl.heads, offsets=offsets, num_partitions=wl.num_partitions,
+                    partition_numel=P, method=method, precision=args.precision, grad_dtype=step_dtype)
+    log(f"workload {wl.name}: {len(wl.shapes)} matrices, {wl.numel / 1e9:.3f} G elements, method {method}, "
+        f"precision {args.precision}, workspace {g.workspace_bytes / 1e9:.1f} GB")
+    mbs, acc, mom = make_inputs(torch, wl, 1000 * wl.config_id)
+    parts_flat = torch.zeros(wl.num_partitions * P, dtype=torch.float32, device="cuda:0")
+    parts = [parts_flat[r * P:(r + 1) * P] for r in range(wl.num_partitions)]
+    ws = torch.empty(g.workspace_bytes, dtype=torch.uint8, device="cuda:0")
+    assert ws.data_ptr() % 256 == 0
+    torch.cuda.synchronize()
+    log("inputs resident")
+
+    def one_step():
+        if acc is not None:
+            for k in range(wl.gas):
+                g.accumulate(acc[1], mbs[k % len(mbs)][1], wl.micro_dtype, k == 0, ws)
+            grads = acc[1]
+        else:
+            grads = mbs[0][1]
+        g.step(grads, mom[1], parts, ws)
+
+    for i in range(args.warmup):
+        one_step()
+        torch.cuda.synchronize()
+        log(f"warmup {i + 1}/{args.warmup} done")
+    g.set_timing(True)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    phases, acc_ms = [], []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev0.record()
+        if acc is not None:
+            for k in range(wl.gas):
+                g.accumulate(acc[1], mbs[k % len(mbs)][1], wl.micro_dtype, k == 0, ws)
+            grads = acc[1]
+        else:
+            grads = mbs[0][1]
+        ev1.record()
+        g.step(grads, mom[1], parts, ws)
+        k1, ns, k3, nl = g.phase_ms()
+        acc_ms.append(ev0.elapsed_time(ev1))
+        phases.append((k1, ns, k3, nl))
+        log(f"step {i + 1}/{args.steps}: K1 {k1:.2f} ms, NS {ns:.2f} ms ({nl} launches), K3 {k3:.2f} ms, "
+            f"accumulate {acc_ms[-1]:.2f} ms")
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    probs = g.problems()
+    nom, sym = ns_flops(probs, method, g.options.ns_steps)
+    k1_ms = statistics.mean(p[0] for p in phases)
+    ns_ms = statistics.mean(p[1] for p in phases)
+    k3_ms = statistics.mean(p[2] for p in phases)
+    nl = phases[-1][3]
+    group_ms = k1_ms + ns_ms + k3_ms
+    numel = wl.numel
+    gsz = 4 if step_dtype == "fp32" else 2
+    xsz = 2 if args.precision == "bf16" else 4
+    k1_bytes = numel * (gsz + 4 + 4 + xsz)          # read G, read m, write m, write X once
+    k3_bytes = numel * (xsz + 4)                     # read X_T, write the fp32 partition
+    acc_bytes = numel * (2 + 4) + (wl.gas - 1) * numel * (2 + 8) if acc is not None else 0
+    peak = PEAK_BF16_TFLOPS if args.precision == "bf16" else PEAK_FP32_TFLOPS
+    ns_tflops_sym = sym / (ns_ms * 1e-3) / 1e12
+    ns_tflops_nom = nom / (ns_ms * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(group_ms, 3),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": args.precision,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "matrices": len(wl.shapes), "numel": numel, "gas": wl.gas,
+                   "partitions": wl.num_partitions, "ns_method": method, "ns_steps": g.options.ns_steps,
+                   "ns_precision": args.precision, "grad_dtype": step_dtype},
+        "phases_ms": {"k1_norm": round(k1_ms, 3), "newton_schulz": round(ns_ms, 3), "k3_scatter": round(k3_ms, 3),
+                      "accumulate": round(statistics.mean(acc_ms), 3) if acc is not None else None},
+        "ns_tflops_nominal": round(ns_tflops_nom, 1),
+        "ns_pct_peak_nominal": round(100 * ns_tflops_nom / peak, 2),
+        "k1_gbs": round(k1_bytes / (k1_ms * 1e-3) / 1e9, 1),
+        "k3_gbs": round(k3_bytes / (k3_ms * 1e-3) / 1e9, 1),
+        "accumulate_gbs": round(acc_bytes / (statistics.mean(acc_ms) * 1e-3) / 1e9, 1) if acc is not None else None,
+        "roofline": {"kernel": "ns_gemm (grouped Newton-Schulz GEMM)", "bound": "mfma",
+                     "achieved": round(ns_tflops_sym, 1), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(ns_tflops_sym / peak, 4), "traffic": None,
+                     "flops_per_step": sym, "launches_per_step": nl,
+                     "avg_launch_ms": round(ns_ms / max(nl, 1), 4)},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on a bounded sample")
+        line["cpu_baseline"] = cpu_baseline(wl, method, nom, args.cpu_budget_s)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+    g.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

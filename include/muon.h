@@ -209,6 +209,16 @@ muon_status muon_plan_runs(const muon_plan *p, int32_t matrix, muon_run *out, in
 muon_status muon_plan_problems(const muon_plan *p, muon_problem_info *out, int32_t cap,
                                int32_t *count);
 
+/* Phase timing.  While enabled, muon_step records HIP events on its stream
+ * around its three phases (K1 with the norm finalisation; all Newton-Schulz
+ * launches; K3), per workspace wave.  muon_plan_phase_ms waits for the last
+ * timed step's events and writes the phase times in milliseconds, summed over
+ * waves: out[0] K1+norm, out[1] Newton-Schulz, out[2] K3; *ns_launches gets
+ * the number of Newton-Schulz launches that step made.  Errors:
+ * INVALID_ARG (NULL plan/out, or no timed step yet), HIP. */
+muon_status muon_plan_set_timing(muon_plan *p, int32_t enable);
+muon_status muon_plan_phase_ms(muon_plan *p, float out[3], int32_t *ns_launches);
+
 void muon_plan_destroy(muon_plan *p);
 const char *muon_status_string(muon_status s);
 const char *muon_last_error(void);

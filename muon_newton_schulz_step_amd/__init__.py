@@ -11,8 +11,8 @@ from __future__ import annotations
 from . import _lib
 from ._lib import (DTYPE, EXPORTS, NS_METHOD, PRECISION, MuonError, load, muon_accumulate,  # noqa: F401
                    muon_default_options, muon_last_error, muon_layout, muon_plan_create, muon_plan_destroy,
-                   muon_plan_problems, muon_plan_runs, muon_plan_stats, muon_plan_workspace_bytes, muon_scatter,
-                   muon_status_string, muon_step)
+                   muon_plan_phase_ms, muon_plan_problems, muon_plan_runs, muon_plan_set_timing, muon_plan_stats,
+                   muon_plan_workspace_bytes, muon_scatter, muon_status_string, muon_step)
 
 __all__ = ["MuonGroup", "pack_layout", "MuonError", "load"] + list(EXPORTS)
 
@@ -85,6 +85,12 @@ class MuonGroup:
 
     def problems(self) -> list:
         return muon_plan_problems(self.plan)
+
+    def set_timing(self, enable: bool = True):
+        muon_plan_set_timing(self.plan, enable)
+
+    def phase_ms(self):
+        return muon_plan_phase_ms(self.plan)
 
     def close(self):
         if getattr(self, "plan", None):

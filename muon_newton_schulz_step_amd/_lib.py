@@ -27,7 +27,8 @@ DTYPE = {"fp32": 0, "bf16": 1}
 # every symbol include/muon.h declares
 EXPORTS = ("muon_default_options", "muon_plan_create", "muon_plan_workspace_bytes", "muon_accumulate",
            "muon_step", "muon_scatter", "muon_plan_stats", "muon_plan_runs", "muon_plan_problems",
-           "muon_plan_destroy", "muon_status_string", "muon_last_error")
+           "muon_plan_set_timing", "muon_plan_phase_ms", "muon_plan_destroy", "muon_status_string",
+           "muon_last_error")
 
 
 class muon_matrix(C.Structure):
@@ -85,6 +86,8 @@ def load(path: str | None = None) -> C.CDLL:
         "muon_plan_stats": (i32, [vp, C.POINTER(muon_stats)]),
         "muon_plan_runs": (i32, [vp, i32, C.POINTER(muon_run), i32, C.POINTER(i32)]),
         "muon_plan_problems": (i32, [vp, C.POINTER(muon_problem_info), i32, C.POINTER(i32)]),
+        "muon_plan_set_timing": (i32, [vp, i32]),
+        "muon_plan_phase_ms": (i32, [vp, C.POINTER(C.c_float), C.POINTER(i32)]),
         "muon_plan_destroy": (None, [vp]),
         "muon_status_string": (C.c_char_p, [i32]),
         "muon_last_error": (C.c_char_p, []),
@@ -204,6 +207,18 @@ def muon_plan_problems(plan) -> list:
     _check(load().muon_plan_problems(plan, arr, n.value, C.byref(n)), "muon_plan_problems")
     return [dict(matrix=q.matrix, head=q.head, m=q.m, n=q.n, transposed=bool(q.transposed), wave=q.wave,
                  flops=q.flops) for q in arr[:n.value]]
+
+
+def muon_plan_set_timing(plan, enable: bool) -> None:
+    _check(load().muon_plan_set_timing(plan, int(bool(enable))), "muon_plan_set_timing")
+
+
+def muon_plan_phase_ms(plan):
+    """(k1_ms, ns_ms, k3_ms, ns_launches) of the last timed step."""
+    out = (C.c_float * 3)()
+    n = C.c_int32()
+    _check(load().muon_plan_phase_ms(plan, out, C.byref(n)), "muon_plan_phase_ms")
+    return float(out[0]), float(out[1]), float(out[2]), int(n.value)
 
 
 def muon_plan_destroy(plan) -> None:

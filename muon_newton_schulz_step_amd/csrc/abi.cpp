@@ -159,6 +159,21 @@ muon_status muon_step(muon_plan *p, const void *const *grads, float *const *mome
   }
   if ((st = upload(p, slot, ws, p->host_tables.size(), s)) != MUON_OK) return st;
 
+  if (p->timing) {
+    const size_t need = 4 * p->waves.size();
+    while (p->phase_events.size() < need) {
+      hipEvent_t ev;
+      hipError_t e = hipEventCreate(&ev);
+      if (e != hipSuccess) return hip_fail(e, "hipEventCreate (timing)");
+      p->phase_events.push_back(ev);
+    }
+  }
+  auto mark = [&](size_t w, int k) -> hipError_t {
+    if (!p->timing) return hipSuccess;
+    return hipEventRecord((hipEvent_t)p->phase_events[4 * w + k], s);
+  };
+  int32_t ns_launches = 0;
+  size_t wi = 0;
   const bool gbf16 = p->opt.grad_dtype == MUON_DT_BF16;
   float *partials = reinterpret_cast<float *>(wsb + p->partials_off);
   float *scales = reinterpret_cast<float *>(wsb + p->scales_off);
@@ -168,9 +183,11 @@ muon_status muon_step(muon_plan *p, const void *const *grads, float *const *mome
     const K1Prob *k1 = reinterpret_cast<const K1Prob *>(wsb + W.off_k1);
     const ProbDev *probs = reinterpret_cast<const ProbDev *>(wsb + W.off_prob);
     const K3Run *runs = reinterpret_cast<const K3Run *>(wsb + W.off_runs);
+    if ((e = mark(wi, 0)) != hipSuccess) return hip_fail(e, "hipEventRecord (timing)");
     if ((e = launch_k1(k1, np, W.k1_tiles, wsb, partials, p->opt.beta, p->opt.nesterov, gbf16, s)) != hipSuccess)
       return hip_fail(e, "K1 launch");
     if ((e = launch_kn(k1, np, partials, scales, p->opt.eps, s)) != hipSuccess) return hip_fail(e, "norm launch");
+    if ((e = mark(wi, 1)) != hipSuccess) return hip_fail(e, "hipEventRecord (timing)");
     if (p->opt.ns_steps == 0) {
       if ((e = launch_kc(probs, k1, np, wsb, scales, s)) != hipSuccess) return hip_fail(e, "copy launch");
     } else {
@@ -184,10 +201,18 @@ muon_status muon_step(muon_plan *p, const void *const *grads, float *const *mome
           GemmArgs a{probs, L.mn ? tmn : tmm, wsb, scales, L.r};
           if ((e = launch_gemm(L.kind == Launch::GEMM_OP, a, L.mn ? nmn : nmm, s)) != hipSuccess)
             return hip_fail(e, "Newton-Schulz launch");
+          ++ns_launches;
         }
       }
     }
+    if ((e = mark(wi, 2)) != hipSuccess) return hip_fail(e, "hipEventRecord (timing)");
     if ((e = launch_k3(runs, (int)W.runs.size(), W.k3_chunks, s)) != hipSuccess) return hip_fail(e, "K3 launch");
+    if ((e = mark(wi, 3)) != hipSuccess) return hip_fail(e, "hipEventRecord (timing)");
+    ++wi;
+  }
+  if (p->timing) {
+    p->timed_step = true;
+    p->timed_launches = ns_launches;
   }
   p->stats.steps += 1;
   p->stats.ns_invocations += (uint64_t)nmat;
@@ -279,8 +304,35 @@ muon_status muon_scatter(muon_plan *p, const void *const *updates, int32_t dtype
   return MUON_OK;
 }
 
+muon_status muon_plan_set_timing(muon_plan *p, int32_t enable) {
+  if (!p) { set_error("muon_plan_set_timing: NULL plan"); return MUON_ERR_INVALID_ARG; }
+  p->timing = enable != 0;
+  p->timed_step = false;
+  return MUON_OK;
+}
+
+muon_status muon_plan_phase_ms(muon_plan *p, float out[3], int32_t *ns_launches) {
+  if (!p || !out) { set_error("muon_plan_phase_ms: NULL argument"); return MUON_ERR_INVALID_ARG; }
+  if (!p->timed_step) { set_error("muon_plan_phase_ms: no timed step yet"); return MUON_ERR_INVALID_ARG; }
+  out[0] = out[1] = out[2] = 0.f;
+  for (size_t w = 0; w < p->waves.size(); ++w) {
+    hipEvent_t *ev = reinterpret_cast<hipEvent_t *>(&p->phase_events[4 * w]);
+    hipError_t e = hipEventSynchronize(ev[3]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize (timing)");
+    for (int k = 0; k < 3; ++k) {
+      float ms = 0.f;
+      e = hipEventElapsedTime(&ms, ev[k], ev[k + 1]);
+      if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+      out[k] += ms;
+    }
+  }
+  if (ns_launches) *ns_launches = p->timed_launches;
+  return MUON_OK;
+}
+
 void muon_plan_destroy(muon_plan *p) {
   if (!p) return;
+  for (void *ev : p->phase_events) (void)hipEventDestroy((hipEvent_t)ev);
   for (int s = 0; s < 2; ++s) {
     if (p->event_live[s]) (void)hipEventSynchronize((hipEvent_t)p->events[s]);
     if (p->staging[s]) (void)hipHostFree(p->staging[s]);

@@ -83,6 +83,11 @@ struct muon_plan {
   void *events[2] = {nullptr, nullptr};
   bool event_live[2] = {false, false};
   int slot = 0;
+  // phase timing (events created lazily; 4 per wave: start, K1 done, NS done, K3 done)
+  bool timing = false;
+  bool timed_step = false;
+  int32_t timed_launches = 0;
+  std::vector<void *> phase_events;
   muon_stats stats{};
 };
 
