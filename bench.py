@@ -168,7 +168,7 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     M.load()
-    wl = W.ALL[args.workload]()
+    wl = W.custom(args.workload) if args.workload.startswith("custom:") else W.ALL[args.workload]()
     method = args.method or wl.methods[0]
     offsets, P = M.pack_layout(wl.shapes, wl.num_partitions, wl.align)
     step_dtype = "fp32" if wl.gas > 1 else wl.micro_dtype

@@ -191,16 +191,19 @@ muon_status muon_step(muon_plan *p, const void *const *grads, float *const *mome
     if (p->opt.ns_steps == 0) {
       if ((e = launch_kc(probs, k1, np, wsb, scales, s)) != hipSuccess) return hip_fail(e, "copy launch");
     } else {
-      // bf16-operand problems first (the bulk of the work), then fp32-operand ones
-      for (int cls = 1; cls >= 0; --cls) {
-        const int nmm = (int)W.tiles_mm[cls].size(), nmn = (int)W.tiles_mn[cls].size();
-        if (nmn == 0) continue;
-        const TileDev *tmm = reinterpret_cast<const TileDev *>(wsb + W.off_tiles_mm[cls]);
-        const TileDev *tmn = reinterpret_cast<const TileDev *>(wsb + W.off_tiles_mn[cls]);
-        for (const Launch &L : p->schedule[cls]) {
-          GemmArgs a{probs, L.mn ? tmn : tmm, wsb, scales, L.r};
-          if ((e = launch_gemm(L.kind == Launch::GEMM_OP, a, L.mn ? nmn : nmm, s)) != hipSuccess)
-            return hip_fail(e, "Newton-Schulz launch");
+      // large bf16 problems first (the bulk of the work), then small bf16
+      // ones, then fp32-operand ones
+      for (int grp = PG_BF16_BIG; grp >= PG_F32; --grp) {
+        if (W.tiles[grp][TL_MN128].empty()) continue;
+        const std::vector<Launch> &sched = p->schedule[grp == PG_F32 ? 0 : 1];
+        for (const Launch &L : sched) {
+          const bool big = grp == PG_BF16_BIG && L.kind == Launch::GEMM_OP;
+          const int list = big ? (L.mn ? TL_MN256 : TL_MM256) : (L.mn ? TL_MN128 : TL_MM128);
+          const TileDev *tl = reinterpret_cast<const TileDev *>(wsb + W.off_tiles[grp][list]);
+          const int nt = (int)W.tiles[grp][list].size();
+          GemmArgs a{probs, tl, wsb, scales, L.r};
+          e = big ? launch_gemm256(a, nt, s) : launch_gemm(L.kind == Launch::GEMM_OP, a, nt, s);
+          if (e != hipSuccess) return hip_fail(e, "Newton-Schulz launch");
           ++ns_launches;
         }
       }

@@ -23,5 +23,6 @@ struct GemmArgs {
   GemmRecipe r;
 };
 hipError_t launch_gemm(bool bf16_operands, const GemmArgs &a, int ntiles, hipStream_t s);
+hipError_t launch_gemm256(const GemmArgs &a, int ntiles, hipStream_t s);
 
 }  // namespace muon

@@ -1,0 +1,490 @@
+// Large-tile grouped Newton-Schulz GEMM for bf16 operands on gfx950.
+//
+// Same contract as ns_gemm (C = s^p (cd D + cacc A B^T) + cdiag I over a
+// tile list, both operands row-major with K contiguous), for problems whose
+// small side is at least 256:
+//  - 256 x 256 output tile per workgroup of 4 wave64s (2 x 2), each wave
+//    128 x 128 = 4 x 4 blocks of v_mfma_f32_32x32x16_bf16, 256 fp32
+//    accumulators per lane.  Per 16-deep K step a wave reads 8 KB of
+//    operands from LDS for 16 MFMAs, half the LDS traffic per flop of a
+//    64 x 64 wave tile.
+//  - K staged 64 deep (128-byte rows) straight from global memory into LDS
+//    with 16-byte LDS-DMA loads (global_load_lds_dwordx4: lane L lands at
+//    base + 16 L), double buffered: the loads of stage t+1 are in flight
+//    while stage t feeds the MFMAs.  A ragged last stage (K not a multiple
+//    of 64) goes through registers so elements at k >= K are zeroed.
+//  - 16-byte chunks of each row are XOR-swizzled (position = chunk ^ f(row))
+//    so the 32 rows a fragment read touches spread over all LDS banks.
+//  - Tiles are taken XCD-major: workgroup i runs on XCD i mod 8, so it is
+//    given tile (i mod 8) * ceil(G/8) + i / 8, which keeps consecutive tiles
+//    of a problem (sharing operand panels) in one XCD's L2.
+// Rows beyond M or N are clamped to the last valid row when loading; they
+// only feed outputs that are never stored.
+#include <hip/hip_runtime.h>
+
+#include "elem.hpp"
+#include "tables.hpp"
+
+#ifndef MUON_LDS_SWIZZLE
+#define MUON_LDS_SWIZZLE 1
+#endif
+#ifndef MUON_XCD_REMAP
+#define MUON_XCD_REMAP 0
+#endif
+#ifndef MUON_BIG_DMA
+#define MUON_BIG_DMA 1
+#endif
+
+namespace muon {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+namespace {
+
+constexpr int BT = 256;            // output tile edge
+constexpr int KS = 64;             // K elements per stage
+constexpr int ROWB = 128;          // bytes per staged row (64 bf16)
+constexpr int OPB = BT * ROWB;     // 32 KB per operand per stage
+constexpr int NTHR = 256;
+constexpr int NXCD = 8;
+constexpr int XCD_CUS = 32;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int swz(int r, int c) {
+#if MUON_LDS_SWIZZLE == 0
+  return c ^ (r & 7);
+#else
+  return c ^ ((r >> 1) & 7);
+#endif
+}
+
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((b >> 16) | 0x40u);
+  b += 0x7fffu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+
+__device__ __forceinline__ void store_elem(char *base, int64_t idx, float v, bool f32) {
+  if (f32) reinterpret_cast<float *>(base)[idx] = v;
+  else reinterpret_cast<uint16_t *>(base)[idx] = f2bf(v);
+}
+
+__device__ __forceinline__ float load_elem(const char *base, int64_t idx, bool f32) {
+  return f32 ? reinterpret_cast<const float *>(base)[idx] : bf2f(reinterpret_cast<const uint16_t *>(base)[idx]);
+}
+
+// Store n (<= 8) consecutive values at element index idx: one 16-byte
+// (bf16) or two 16-byte (fp32) stores when the chunk is whole and aligned,
+// element stores otherwise.
+__device__ __forceinline__ void store_chunk(char *base, int64_t idx, const float *v, int n, bool f32) {
+  if (f32) {
+    float *p = reinterpret_cast<float *>(base) + idx;
+    if (n == 8 && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+      *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4 *>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    } else {
+      for (int e = 0; e < n; ++e) p[e] = v[e];
+    }
+  } else {
+    uint16_t *p = reinterpret_cast<uint16_t *>(base) + idx;
+    if (n == 8 && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+      uint4 w;
+      w.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+      w.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+      w.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
+      w.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+      *reinterpret_cast<uint4 *>(p) = w;
+    } else {
+      for (int e = 0; e < n; ++e) p[e] = f2bf(v[e]);
+    }
+  }
+}
+
+// Store / load n (<= 4) consecutive values: one vector access (8 bytes
+// bf16, 16 bytes fp32) when the quad is whole and aligned, elements otherwise.
+__device__ __forceinline__ void store_quad(char *base, int64_t idx, const float *v, int n, bool f32) {
+  if (f32) {
+    float *p = reinterpret_cast<float *>(base) + idx;
+    if (n == 4 && (reinterpret_cast<uintptr_t>(p) & 15) == 0) *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    else for (int e = 0; e < n; ++e) p[e] = v[e];
+  } else {
+    uint16_t *p = reinterpret_cast<uint16_t *>(base) + idx;
+    if (n == 4 && (reinterpret_cast<uintptr_t>(p) & 7) == 0) {
+      uint2 w;
+      w.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+      w.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+      *reinterpret_cast<uint2 *>(p) = w;
+    } else {
+      for (int e = 0; e < n; ++e) p[e] = f2bf(v[e]);
+    }
+  }
+}
+
+__device__ __forceinline__ void load_quad(const char *base, int64_t idx, float *v, int n, bool f32) {
+  if (f32) {
+    const float *p = reinterpret_cast<const float *>(base) + idx;
+    if (n == 4 && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+      const float4 w = *reinterpret_cast<const float4 *>(p);
+      v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+    } else {
+      for (int e = 0; e < n; ++e) v[e] = p[e];
+    }
+  } else {
+    const uint16_t *p = reinterpret_cast<const uint16_t *>(base) + idx;
+    if (n == 4 && (reinterpret_cast<uintptr_t>(p) & 7) == 0) {
+      const uint2 w = *reinterpret_cast<const uint2 *>(p);
+      v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xffff0000u);
+      v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xffff0000u);
+    } else {
+      for (int e = 0; e < n; ++e) v[e] = bf2f(p[e]);
+    }
+  }
+}
+
+__device__ __forceinline__ uint4 mask_tail_bf16(uint4 v, int valid) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t keep = (2 * d < valid ? 0x0000ffffu : 0u) | (2 * d + 1 < valid ? 0xffff0000u : 0u);
+    w[d] &= keep;
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles) {
+  __shared__ __attribute__((aligned(1024))) char lds[2 * 2 * OPB];
+
+#if MUON_XCD_REMAP
+  // Workgroup i runs on XCD i % 8.  The tile list is cut into chunks of
+  // 8 x 32 tiles; XCD x takes tiles [32 x, 32 x + 32) of each chunk, i.e.
+  // about two tile-rows of one problem, so the 32 CUs of an XCD share their
+  // operand panels through its L2 while all XCDs stay on the same problem.
+  const int xcd = (int)(blockIdx.x % NXCD), slot = (int)(blockIdx.x / NXCD);
+  const int t = (slot / XCD_CUS) * (NXCD * XCD_CUS) + xcd * XCD_CUS + slot % XCD_CUS;
+  if (t >= ntiles) return;
+#else
+  const int t = blockIdx.x;
+#endif
+  const TileDev tile = args.tiles[t];
+  const ProbDev &P = args.probs[tile.prob];
+  const GemmRecipe R = args.r;
+  const int64_t M = R.dimM ? P.n : P.m;
+  const int64_t N = R.dimN ? P.n : P.m;
+  const int64_t K = R.dimK ? P.n : P.m;
+  const char *A = args.ws + P.off[R.rA];
+  const char *B = args.ws + P.off[R.rB];
+  const int64_t lda = P.ld[R.rA], ldb = P.ld[R.rB];
+  const int64_t m0 = (int64_t)tile.tm * BT, n0 = (int64_t)tile.tn * BT;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 31, lg = lane >> 5;
+
+  // loader geometry: wave w stages rows [64 w, 64 w + 64) of both operands,
+  // 8 rows (1 KB) per instruction; lane L covers row 64w + 8j + L/8, LDS
+  // chunk position L%8, which holds global chunk swz(row, L%8).
+  const int lrow = lane >> 3, lpos = lane & 7;
+  int64_t arow[8], brow[8];
+  int lchunk[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = wave * 64 + j * 8 + lrow;
+    arow[j] = min(m0 + r, M - 1) * lda;
+    brow[j] = min(n0 + r, N - 1) * ldb;
+    lchunk[j] = swz(r, lpos) * 8;
+  }
+  const int nfull = (int)(K / KS);
+  const int nk = (int)((K + KS - 1) / KS);
+
+  auto dma_stage = [&](int kt, int st) {
+    const int64_t k0 = (int64_t)kt * KS;
+    char *la = lds + st * 2 * OPB;
+    char *lb = la + OPB;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int off = (wave * 64 + j * 8) * ROWB;
+      __builtin_amdgcn_global_load_lds(A + (arow[j] + k0 + lchunk[j]) * 2, (lds_void *)(la + off), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(B + (brow[j] + k0 + lchunk[j]) * 2, (lds_void *)(lb + off), 16, 0, 0);
+    }
+  };
+  auto reg_stage = [&](int kt, int st) {
+    const int64_t k0 = (int64_t)kt * KS;
+    char *la = lds + st * 2 * OPB;
+    char *lb = la + OPB;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t gk = k0 + lchunk[j];
+      const int valid = (int)min<int64_t>(K - gk, 8);
+      uint4 va = make_uint4(0, 0, 0, 0), vb = make_uint4(0, 0, 0, 0);
+      if (valid > 0) {
+        va = *reinterpret_cast<const uint4 *>(A + (arow[j] + gk) * 2);
+        vb = *reinterpret_cast<const uint4 *>(B + (brow[j] + gk) * 2);
+        if (valid < 8) { va = mask_tail_bf16(va, valid); vb = mask_tail_bf16(vb, valid); }
+      }
+      const int off = (wave * 64 + j * 8) * ROWB + lane * 16;
+      *reinterpret_cast<uint4 *>(la + off) = va;
+      *reinterpret_cast<uint4 *>(lb + off) = vb;
+    }
+  };
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  // fragment row offsets (bytes) and the per-row swizzle key
+  int arb[4], brb[4], ak[4], bk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ra_ = wm * 128 + i * 32 + lr, rb_ = wn * 128 + i * 32 + lr;
+    arb[i] = ra_ * ROWB; ak[i] = ra_;
+    brb[i] = rb_ * ROWB; bk[i] = rb_;
+  }
+  auto compute = [&](int st) {
+    const char *la = lds + st * 2 * OPB;
+    const char *lb = la + OPB;
+#pragma unroll
+    for (int ks = 0; ks < KS / 16; ++ks) {
+      const int c = ks * 2 + lg;
+      bf16x8_t a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8_t *>(la + arb[i] + swz(ak[i], c) * 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const bf16x8_t *>(lb + brb[j] + swz(bk[j], c) * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+#if MUON_BIG_DMA
+  // Software pipeline over 16-deep k-steps: the fragments of step s+1 are
+  // read from LDS while the 16 MFMAs of step s run (two fragment sets).
+  // The stage barrier sits before the last k-step of each stage, so the
+  // first reads of the next stage overlap that step's MFMAs, and the
+  // LDS-DMA of stage t+2 is issued as soon as stage t's buffer is free.
+  bf16x8_t fa[2][4], fb[2][4];
+  auto read_frags = [&](int set, int st, int ks) {
+    const char *la = lds + st * 2 * OPB;
+    const char *lb = la + OPB;
+    const int c = ks * 2 + lg;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[set][i] = *reinterpret_cast<const bf16x8_t *>(la + arb[i] + swz(ak[i], c) * 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[set][j] = *reinterpret_cast<const bf16x8_t *>(lb + brb[j] + swz(bk[j], c) * 16);
+  };
+  auto mfmas = [&](int set) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
+  };
+  auto interleave = [&]() {
+    // 16 MFMAs with the 8 fragment reads of the next step between them
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+  if (nfull > 0) dma_stage(0, 0);
+  else reg_stage(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (nk > 1) {
+    if (1 < nfull) dma_stage(1, 1);
+    else reg_stage(1, 1);
+  }
+  read_frags(0, 0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    // k-steps 0..2: MFMAs of step s, reads of step s+1 (same stage)
+    read_frags(1, st, 1);
+    mfmas(0);
+    interleave();
+    read_frags(0, st, 2);
+    mfmas(1);
+    interleave();
+    read_frags(1, st, 3);
+    mfmas(0);
+    interleave();
+    // stage t+1 landed and every wave is done reading stage t: sync, then
+    // refill buffer st with stage t+2 and start reading stage t+1
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kt + 2 < nk) {
+      if (kt + 2 < nfull) dma_stage(kt + 2, st);
+      else reg_stage(kt + 2, st);
+    }
+    if (kt + 1 < nk) read_frags(0, st ^ 1, 0);
+    mfmas(1);
+    interleave();
+  }
+#else
+  // register-staged: the next stage's global loads are in flight in VGPRs
+  // while the current stage feeds the MFMAs, then written to the other LDS
+  // buffer; one barrier per stage.
+  uint4 ra[8], rb[8];
+  auto gload = [&](int kt) {
+    const int64_t k0 = (int64_t)kt * KS;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t gk = k0 + lchunk[j];
+      const int valid = (int)min<int64_t>(K - gk, 8);
+      uint4 va = make_uint4(0, 0, 0, 0), vb = make_uint4(0, 0, 0, 0);
+      if (valid > 0) {
+        va = *reinterpret_cast<const uint4 *>(A + (arow[j] + gk) * 2);
+        vb = *reinterpret_cast<const uint4 *>(B + (brow[j] + gk) * 2);
+        if (valid < 8) { va = mask_tail_bf16(va, valid); vb = mask_tail_bf16(vb, valid); }
+      }
+      ra[j] = va;
+      rb[j] = vb;
+    }
+  };
+  auto lstore = [&](int st) {
+    char *la = lds + st * 2 * OPB;
+    char *lb = la + OPB;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int off = (wave * 64 + j * 8) * ROWB + lane * 16;
+      *reinterpret_cast<uint4 *>(la + off) = ra[j];
+      *reinterpret_cast<uint4 *>(lb + off) = rb[j];
+    }
+  };
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    const bool more = kt + 1 < nk;
+    if (more) gload(kt + 1);
+    compute(st);
+    if (more) lstore(st ^ 1);
+    __syncthreads();
+  }
+#endif
+
+  // ---- epilogue: C = s^p (cd D + cacc acc) + cdiag I, stored to S0/S1.
+  // The tile leaves registers in four passes of 64 rows (block row p of
+  // both wave rows), staged as fp32 in LDS with row stride 264 floats (the
+  // two half-waves of an accumulator write land in opposite bank halves):
+  //   phase 1: accumulators -> LDS (times cacc)
+  //   phase 2: 4-float row quads (a wave touches 1 KB contiguous): + cd D
+  //            (vector reads of D), scale, diagonal; final values back to
+  //            LDS; row-major stores.  Runs even when every output is
+  //            transposed, since it produces the final values.
+  //   phase 3: 8-row column chunks -> transposed stores and the mirror tile
+  //            of symmetric outputs (16 bytes per lane for bf16)
+  __syncthreads();
+  float *stg = reinterpret_cast<float *>(lds);
+  constexpr int SLD = 264;  // staging row stride (floats)
+  float sc = 1.f;
+  if (R.scale_pow) {
+    const float sv = args.scales[tile.prob];
+    sc = R.scale_pow == 2 ? sv * sv : sv;
+  }
+  const bool mirror = (R.flags & GF_SYM) && tile.tm != tile.tn;
+  const bool t0 = (R.flags & GF_S0_TRANS) || ((R.flags & GF_S0_PROBT) && (P.flags & PF_TALL));
+  const bool t1 = (R.flags & GF_S1_TRANS) != 0;
+  const bool f0 = (R.flags & GF_S0_F32) != 0, f1 = (R.flags & GF_S1_F32) != 0, fd = (R.flags & GF_D_F32) != 0;
+  const bool diag = (R.flags & GF_DIAG) != 0;
+  const char *D = R.rD >= 0 ? args.ws + P.off[R.rD] : nullptr;
+  const int64_t ldd = R.rD >= 0 ? P.ld[R.rD] : 0;
+  char *S0 = args.ws + P.off[R.rS0];
+  const int64_t ld0 = P.ld[R.rS0];
+  char *S1 = R.rS1 >= 0 ? args.ws + P.off[R.rS1] : nullptr;
+  const int64_t ld1 = R.rS1 >= 0 ? P.ld[R.rS1] : 0;
+  const bool col_phase = t0 || (S1 && t1) || mirror;
+
+  auto put = [&](const f32x16_t &blk, int j) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = wm * 32 + 8 * (v >> 2) + 4 * lg + (v & 3);
+      stg[r * SLD + wn * 128 + j * 32 + lr] = blk[v] * R.cacc;
+    }
+  };
+#pragma unroll 1
+  for (int p = 0; p < 4; ++p) {
+    if (p) __syncthreads();
+    if (p == 0) { put(acc[0][0], 0); put(acc[0][1], 1); put(acc[0][2], 2); put(acc[0][3], 3); }
+    if (p == 1) { put(acc[1][0], 0); put(acc[1][1], 1); put(acc[1][2], 2); put(acc[1][3], 3); }
+    if (p == 2) { put(acc[2][0], 0); put(acc[2][1], 1); put(acc[2][2], 2); put(acc[2][3], 3); }
+    if (p == 3) { put(acc[3][0], 0); put(acc[3][1], 1); put(acc[3][2], 2); put(acc[3][3], 3); }
+    __syncthreads();
+    // staging row r (0..63) is tile row (r / 32) * 128 + p * 32 + r % 32
+#pragma unroll 1
+    for (int q = 0; q < 16; ++q) {
+      const int ch = tid + NTHR * q;        // 4096 quads: 64 rows x 64 quads
+      const int r = ch >> 6, c4 = (ch & 63) * 4;
+      const int64_t gi = m0 + (r >> 5) * 128 + p * 32 + (r & 31);
+      const int64_t gj = n0 + c4;
+      float *src = stg + r * SLD + c4;
+      float4 v4 = *reinterpret_cast<const float4 *>(src);
+      float v[4] = {v4.x, v4.y, v4.z, v4.w};
+      if (gi < M) {
+        const int nv = (int)min<int64_t>(N - gj, 4);
+        float dv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (D && nv > 0) load_quad(D, gi * ldd + gj, dv, nv, fd);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float x = v[e];
+          if (D) x = fmaf(R.cd, dv[e], x);
+          x *= sc;
+          if (diag && gi == gj + e) x += R.cdiag;
+          v[e] = x;
+        }
+        if (col_phase) *reinterpret_cast<float4 *>(src) = make_float4(v[0], v[1], v[2], v[3]);
+        if (nv > 0) {
+          if (!t0) store_quad(S0, gi * ld0 + gj, v, nv, f0);
+          if (S1 && !t1) store_quad(S1, gi * ld1 + gj, v, nv, f1);
+        }
+      }
+    }
+    if (col_phase) {
+      __syncthreads();
+#pragma unroll 1
+      for (int q = 0; q < 8; ++q) {
+        const int ch = tid + NTHR * q;      // 2048 chunks: 256 columns x 8 row chunks
+        const int c = ch & 255, r8 = (ch >> 8) * 8;
+        const int64_t gj = n0 + c;
+        const int64_t gi = m0 + (r8 >> 5) * 128 + p * 32 + (r8 & 31);
+        if (gj >= N) continue;
+        const int nv = (int)min<int64_t>(M - gi, 8);
+        if (nv <= 0) continue;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = stg[(r8 + e) * SLD + c];
+        if (t0 || mirror) store_chunk(S0, gj * ld0 + gi, v, nv, f0);
+        if (S1 && (t1 || mirror)) store_chunk(S1, gj * ld1 + gi, v, nv, f1);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm256(const GemmArgs &a, int ntiles, hipStream_t s) {
+  if (ntiles <= 0) return hipSuccess;
+#if MUON_XCD_REMAP
+  const int chunk = NXCD * XCD_CUS;
+  const int grid = (ntiles + chunk - 1) / chunk * chunk;
+  hipLaunchKernelGGL(ns_gemm256, dim3(grid), dim3(NTHR), 0, s, a, ntiles);
+#else
+  hipLaunchKernelGGL(ns_gemm256, dim3(ntiles), dim3(NTHR), 0, s, a, ntiles);
+#endif
+  return hipGetLastError();
+}
+
+}  // namespace muon

@@ -248,7 +248,8 @@ muon_status build_plan(muon_plan *p) {
   for (size_t w = 0; w < p->waves.size(); ++w) {
     WavePlan &W = p->waves[w];
     W.probs.clear(); W.k1.clear(); W.runs.clear(); W.run_src.clear(); W.k1_matrix.clear();
-    for (int c = 0; c < 2; ++c) { W.tiles_mm[c].clear(); W.tiles_mn[c].clear(); }
+    for (int g = 0; g < NGROUPS; ++g)
+      for (int l = 0; l < NLISTS; ++l) W.tiles[g][l].clear();
     int32_t k1t = 0;
     for (size_t li = 0; li < W.problems.size(); ++li) {
       const ProblemPlan &q = p->probs[W.problems[li]];
@@ -300,12 +301,16 @@ muon_status build_plan(muon_plan *p) {
       W.k1.push_back(k);
       W.k1_matrix.push_back(q.matrix);
 
-      const int cls = M.ops32 ? 0 : 1;
-      const int64_t tmn = cdiv(q.m, GEMM_TILE), tnn = cdiv(q.n, GEMM_TILE);
-      for (int64_t a = 0; a < tmn; ++a)
-        for (int64_t b = a; b < tmn; ++b) W.tiles_mm[cls].push_back(TileDev{(int32_t)li, (int16_t)a, (int16_t)b});
-      for (int64_t a = 0; a < tmn; ++a)
-        for (int64_t b = 0; b < tnn; ++b) W.tiles_mn[cls].push_back(TileDev{(int32_t)li, (int16_t)a, (int16_t)b});
+      const int grp = M.ops32 ? PG_F32 : (q.m >= BIG_TILE_MIN_M ? PG_BF16_BIG : PG_BF16);
+      auto add_tiles = [&](int tile, int lmm, int lmn) {
+        const int64_t tmn = cdiv(q.m, tile), tnn = cdiv(q.n, tile);
+        for (int64_t a = 0; a < tmn; ++a)
+          for (int64_t b = a; b < tmn; ++b) W.tiles[grp][lmm].push_back(TileDev{(int32_t)li, (int16_t)a, (int16_t)b});
+        for (int64_t a = 0; a < tmn; ++a)
+          for (int64_t b = 0; b < tnn; ++b) W.tiles[grp][lmn].push_back(TileDev{(int32_t)li, (int16_t)a, (int16_t)b});
+      };
+      add_tiles(GEMM_TILE, TL_MM128, TL_MN128);
+      if (grp == PG_BF16_BIG) add_tiles(BIG_TILE, TL_MM256, TL_MN256);
     }
     W.k1_tiles = k1t;
     max_k1 = std::max<int64_t>(max_k1, k1t);
@@ -325,10 +330,8 @@ muon_status build_plan(muon_plan *p) {
     W.k3_chunks = ch;
     W.off_prob = tab.take((int64_t)W.probs.size() * sizeof(ProbDev));
     W.off_k1 = tab.take((int64_t)W.k1.size() * sizeof(K1Prob));
-    for (int c = 0; c < 2; ++c) {
-      W.off_tiles_mm[c] = tab.take((int64_t)W.tiles_mm[c].size() * sizeof(TileDev));
-      W.off_tiles_mn[c] = tab.take((int64_t)W.tiles_mn[c].size() * sizeof(TileDev));
-    }
+    for (int g = 0; g < NGROUPS; ++g)
+      for (int l = 0; l < NLISTS; ++l) W.off_tiles[g][l] = tab.take((int64_t)W.tiles[g][l].size() * sizeof(TileDev));
     W.off_runs = tab.take((int64_t)W.runs.size() * sizeof(K3Run));
   }
   // the accumulation and scatter tables reuse the head of the table region
@@ -359,10 +362,9 @@ muon_status build_plan(muon_plan *p) {
     char *h = p->host_tables.data();
     std::memcpy(h + W.off_prob, W.probs.data(), W.probs.size() * sizeof(ProbDev));
     std::memcpy(h + W.off_k1, W.k1.data(), W.k1.size() * sizeof(K1Prob));
-    for (int c = 0; c < 2; ++c) {
-      std::memcpy(h + W.off_tiles_mm[c], W.tiles_mm[c].data(), W.tiles_mm[c].size() * sizeof(TileDev));
-      std::memcpy(h + W.off_tiles_mn[c], W.tiles_mn[c].data(), W.tiles_mn[c].size() * sizeof(TileDev));
-    }
+    for (int g = 0; g < NGROUPS; ++g)
+      for (int l = 0; l < NLISTS; ++l)
+        std::memcpy(h + W.off_tiles[g][l], W.tiles[g][l].data(), W.tiles[g][l].size() * sizeof(TileDev));
     std::memcpy(h + W.off_runs, W.runs.data(), W.runs.size() * sizeof(K3Run));
   }
   return MUON_OK;

@@ -44,11 +44,12 @@ struct WavePlan {
   std::vector<int32_t> problems;  // global ids in LPT order (wave-local index = position)
   int64_t data_bytes = 0;
   // byte offsets of this wave's tables inside the workspace
-  // tile lists per operand class: [0] fp32 operands, [1] bf16 operands
-  int64_t off_prob = 0, off_k1 = 0, off_tiles_mm[2] = {0, 0}, off_tiles_mn[2] = {0, 0}, off_runs = 0;
+  // tile lists per problem group and list kind (ProbGroup x TileList)
+  int64_t off_prob = 0, off_k1 = 0, off_runs = 0;
+  int64_t off_tiles[NGROUPS][NLISTS] = {};
   std::vector<ProbDev> probs;
   std::vector<K1Prob> k1;
-  std::vector<TileDev> tiles_mm[2], tiles_mn[2];
+  std::vector<TileDev> tiles[NGROUPS][NLISTS];
   std::vector<K3Run> runs;
   std::vector<muon_run> run_src;     // the owned run behind each K3 entry (to patch pointers)
   std::vector<int32_t> k1_matrix;    // matrix of each K1 problem

@@ -24,9 +24,20 @@ enum Role : int {
   NROLES
 };
 
-// Output tile edge of the grouped GEMMs (square tiles; symmetric outputs list
-// only tm <= tn).
+// Output tile edges of the grouped GEMMs (square tiles; symmetric outputs
+// list only tm <= tn).  bf16 problems whose small side reaches BIG_TILE use
+// the large-tile kernel.
 constexpr int GEMM_TILE = 128;
+constexpr int BIG_TILE = 256;
+#ifndef MUON_BIG_TILE_MIN_M
+#define MUON_BIG_TILE_MIN_M 256
+#endif
+constexpr int BIG_TILE_MIN_M = MUON_BIG_TILE_MIN_M;
+
+// Problem groups of a wave: fp32 operands; bf16 with m < BIG_TILE; bf16 with
+// m >= BIG_TILE.  Tile lists per group: m x m and m x n, at each tile size.
+enum ProbGroup : int { PG_F32 = 0, PG_BF16 = 1, PG_BF16_BIG = 2, NGROUPS };
+enum TileList : int { TL_MM128 = 0, TL_MN128, TL_MM256, TL_MN256, NLISTS };
 
 // Newton-Schulz blocks whose small side is below this run on fp32 operands
 // even when bf16 is asked for: with few rows, the bf16 rounding of the m x m

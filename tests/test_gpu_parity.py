@@ -255,3 +255,24 @@ def test_per_head_toggle_changes_only_tagged():
     n0 = 256 * 128
     assert not np.array_equal(fa[:n0], fb[:n0])
     np.testing.assert_array_equal(fa[n0:n0 + 128 * 384].view(np.uint32), fb[n0:n0 + 128 * 384].view(np.uint32))
+
+
+# --------------------------------------------- large-tile kernel (m >= 256)
+
+BIG_SHAPES = [(512, 700), (700, 300), (256, 256), (600, 1100), (1024, 512)]
+
+
+@pytest.mark.parametrize("method", ["standard", "gram"])
+def test_big_tile_group(method):
+    # small sides 256..600 with ragged M/N/K against the 256-wide tiles and
+    # the 64-deep K stages (700 = 10*64 + 60, 1100 = 17*64 + 12)
+    offsets, P = O.pack_layout(BIG_SHAPES, 2, 16)
+    g = M.MuonGroup(BIG_SHAPES, offsets=offsets, num_partitions=2, partition_numel=P, method=method,
+                    precision="bf16", grad_dtype="bf16")
+    micro = _micro(BIG_SHAPES, "bf16", 0.02, 1, 1, cid=41)
+    parts, moms = run_steps(g, micro, "bf16", use_accumulate=False)
+    res, state = _oracle_run(BIG_SHAPES, [0] * len(BIG_SHAPES), offsets, 2, P, micro, "bf16", method)
+    worst = _compare(BIG_SHAPES, offsets, parts, res, TOL["bf16"], f"big/{method}")
+    print(f"big-tile bf16 {method}: worst rel err {worst:.3e}")
+    _check_padding(parts, BIG_SHAPES, offsets, P)
+    _check_momentum(moms, state, res)

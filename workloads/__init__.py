@@ -152,4 +152,22 @@ def share70b(layers: int = 8) -> Workload:
         num_partitions=1, methods=("standard", "gram"), layer_kinds=kinds)
 
 
+def custom(spec: str) -> Workload:
+    """A synthetic group from a spec "custom:RxC*N[/H],RxC*N,..." (N copies of
+    a rows x cols matrix, optionally split into H heads); bf16 N(0, 0.02^2)
+    grads, one step, one partition."""
+    shapes, heads = [], []
+    for part in spec.split(":", 1)[1].split(","):
+        h = 0
+        if "/" in part:
+            part, hs = part.split("/")
+            h = int(hs)
+        dims, _, cnt = part.partition("*")
+        r, c = (int(v) for v in dims.split("x"))
+        for _ in range(int(cnt or 1)):
+            shapes.append((r, c)); heads.append(h)
+    return Workload(name=spec, config_id=9, shapes=shapes, heads=heads, grad_dtype="bf16", micro_dtype="bf16",
+                    sigma=0.02, gas=1, steps=1, num_partitions=1, methods=("standard", "gram"))
+
+
 ALL = {w().name: w for w in (tiny, h1024, per_head, llama7b, share70b)}
