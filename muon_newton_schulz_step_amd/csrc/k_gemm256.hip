@@ -15,9 +15,14 @@
 //    of 64) goes through registers so elements at k >= K are zeroed.
 //  - 16-byte chunks of each row are XOR-swizzled (position = chunk ^ f(row))
 //    so the 32 rows a fragment read touches spread over all LDS banks.
-//  - Tiles are taken XCD-major: workgroup i runs on XCD i mod 8, so it is
-//    given tile (i mod 8) * ceil(G/8) + i / 8, which keeps consecutive tiles
-//    of a problem (sharing operand panels) in one XCD's L2.
+//  - Workgroup i runs on XCD i mod 8; the tile list (ordered in 4 x 8
+//    blocks per problem) is cut into chunks of 256 and XCD x takes entries
+//    [32 x, 32 x + 32) of each chunk, so the 32 CUs of an XCD work on one
+//    block and share its operand panels in their L2 (measured L2 hit rate
+//    of the stage loads is otherwise about 50%).
+//  - MUON_BIG_RING (default 0) selects an alternative pipeline with a ring
+//    of 32-deep stages; measured slower on MI355X than the two 64-deep
+//    buffers, kept for study.
 // Rows beyond M or N are clamped to the last valid row when loading; they
 // only feed outputs that are never stored.
 #include <hip/hip_runtime.h>
@@ -29,10 +34,13 @@
 #define MUON_LDS_SWIZZLE 1
 #endif
 #ifndef MUON_XCD_REMAP
-#define MUON_XCD_REMAP 0
+#define MUON_XCD_REMAP 1
 #endif
 #ifndef MUON_BIG_DMA
 #define MUON_BIG_DMA 1
+#endif
+#ifndef MUON_BIG_RING
+#define MUON_BIG_RING 0
 #endif
 
 namespace muon {
@@ -157,7 +165,11 @@ __device__ __forceinline__ uint4 mask_tail_bf16(uint4 v, int valid) {
 }
 
 __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles) {
+#if MUON_BIG_RING * 32768 > 131072
+  __shared__ __attribute__((aligned(1024))) char lds[MUON_BIG_RING * 32768];
+#else
   __shared__ __attribute__((aligned(1024))) char lds[2 * 2 * OPB];
+#endif
 
 #if MUON_XCD_REMAP
   // Workgroup i runs on XCD i % 8.  The tile list is cut into chunks of
@@ -268,7 +280,129 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
     }
   };
 
-#if MUON_BIG_DMA
+#if MUON_BIG_RING
+  // Ring of MUON_BIG_RING stages, each 32 deep (64-byte rows, 4 chunks,
+  // position = chunk ^ ((row >> 2) & 3)), filled by LDS-DMA up to RING-1
+  // stages ahead.  Each stage is two 16-deep k-steps; the barrier sits
+  // before the second one.  At the barrier of stage t only the DMA of stage
+  // t+1 must have landed (vmcnt may still count RING-2 later stages).
+  constexpr int RS = 32;                // K elements per ring stage
+  constexpr int RROW = 64;              // bytes per staged row
+  constexpr int ROP = BT * RROW;        // 16 KB per operand per stage
+  constexpr int NB = MUON_BIG_RING;
+  static_assert(NB * 2 * ROP <= (int)sizeof(lds), "ring exceeds the LDS allocation");
+  auto rswz = [](int r, int c) { return c ^ ((r >> 2) & 3); };
+  // loader: wave w stages rows [64 w, 64 w + 64), 16 rows (1 KB) per
+  // instruction; lane L covers row 64w + 16j + L/4, position L%4
+  int64_t rar[4], rbr[4];
+  int rch[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = wave * 64 + j * 16 + (lane >> 2);
+    rar[j] = min(m0 + r, M - 1) * lda;
+    rbr[j] = min(n0 + r, N - 1) * ldb;
+    rch[j] = rswz(r, lane & 3) * 8;
+  }
+  const int rnfull = (int)(K / RS);
+  const int rnk = (int)((K + RS - 1) / RS);
+  // half h (0/1) of stage kt: A and B rows j = 2h, 2h+1 of this wave
+  // (4 DMA instructions); a ragged stage is staged whole, through
+  // registers, by its first half
+  auto ring_half = [&](int kt, int h) {
+    const int64_t k0 = (int64_t)kt * RS;
+    char *la = lds + (kt % NB) * 2 * ROP;
+    char *lb = la + ROP;
+    if (kt < rnfull) {
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * h + jj;
+        const int off = (wave * 64 + j * 16) * RROW;
+        __builtin_amdgcn_global_load_lds(A + (rar[j] + k0 + rch[j]) * 2, (lds_void *)(la + off), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(B + (rbr[j] + k0 + rch[j]) * 2, (lds_void *)(lb + off), 16, 0, 0);
+      }
+    } else if (h == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t gk = k0 + rch[j];
+        const int valid = (int)min<int64_t>(K - gk, 8);
+        uint4 va = make_uint4(0, 0, 0, 0), vb = make_uint4(0, 0, 0, 0);
+        if (valid > 0) {
+          va = *reinterpret_cast<const uint4 *>(A + (rar[j] + gk) * 2);
+          vb = *reinterpret_cast<const uint4 *>(B + (rbr[j] + gk) * 2);
+          if (valid < 8) { va = mask_tail_bf16(va, valid); vb = mask_tail_bf16(vb, valid); }
+        }
+        const int off = (wave * 64 + j * 16) * RROW + lane * 16;
+        *reinterpret_cast<uint4 *>(la + off) = va;
+        *reinterpret_cast<uint4 *>(lb + off) = vb;
+      }
+    }
+  };
+  int rab[4], rbb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    rab[i] = (wm * 128 + i * 32 + lr) * RROW;
+    rbb[i] = (wn * 128 + i * 32 + lr) * RROW;
+  }
+  bf16x8_t fa[2][4], fb[2][4];
+  auto read_frags = [&](int set, int kt, int ks) {
+    const char *la = lds + (kt % NB) * 2 * ROP;
+    const char *lb = la + ROP;
+    const int c = ks * 2 + lg;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[set][i] = *reinterpret_cast<const bf16x8_t *>(la + rab[i] + rswz(ak[i], c) * 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[set][j] = *reinterpret_cast<const bf16x8_t *>(lb + rbb[j] + rswz(bk[j], c) * 16);
+  };
+  auto mfmas = [&](int set) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
+  };
+  // 16 MFMAs with the 8 fragment reads of the next k-step and the 4 DMA
+  // instructions of half a stage spread between them
+  auto interleave = [&]() {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+  (void)nfull; (void)nk;
+  for (int t = 0; t < NB - 1 && t < rnk; ++t) { ring_half(t, 0); ring_half(t, 1); }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // prologue: keep it simple
+  __syncthreads();
+  read_frags(0, 0, 0);
+  for (int kt = 0; kt < rnk; ++kt) {
+    // stage kt+NB-1 goes into the buffer of stage kt-1, free since the
+    // barrier of stage kt-1; its two halves are issued across this stage
+    const int sn = kt + NB - 1;
+    read_frags(1, kt, 1);
+    if (sn < rnk) ring_half(sn, 0);
+    mfmas(0);
+    interleave();
+    // Issued so far: stages <= kt+NB-2 and half of stage kt+NB-1.  Stage
+    // kt+1 must have landed; stages kt+2 .. kt+NB-2 (8 DMA instructions
+    // each) and the first half of kt+NB-1 (4) may be in flight.  Loads
+    // complete in issue order for vmcnt.
+    if (sn < rnfull) {
+      if constexpr (NB == 5) asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+      else if constexpr (NB == 4) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
+    if (sn < rnk) ring_half(sn, 1);
+    if (kt + 1 < rnk) read_frags(0, kt + 1, 0);
+    mfmas(1);
+    interleave();
+  }
+#elif MUON_BIG_DMA
   // Software pipeline over 16-deep k-steps: the fragments of step s+1 are
   // read from LDS while the 16 MFMAs of step s run (two fragment sets).
   // The stage barrier sits before the last k-step of each stage, so the
@@ -333,9 +467,33 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
     interleave();
   }
 #else
-  // register-staged: the next stage's global loads are in flight in VGPRs
-  // while the current stage feeds the MFMAs, then written to the other LDS
-  // buffer; one barrier per stage.
+  // Register-staged variant of the same pipeline: the global loads of stage
+  // t+2 are issued into VGPRs right after the barrier of stage t and written
+  // to the free LDS buffer just before the next barrier.
+  bf16x8_t fa[2][4], fb[2][4];
+  auto read_frags = [&](int set, int st, int ks) {
+    const char *la = lds + st * 2 * OPB;
+    const char *lb = la + OPB;
+    const int c = ks * 2 + lg;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[set][i] = *reinterpret_cast<const bf16x8_t *>(la + arb[i] + swz(ak[i], c) * 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[set][j] = *reinterpret_cast<const bf16x8_t *>(lb + brb[j] + swz(bk[j], c) * 16);
+  };
+  auto mfmas = [&](int set) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
+  };
+  auto interleave = [&]() {
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
   uint4 ra[8], rb[8];
   auto gload = [&](int kt) {
     const int64_t k0 = (int64_t)kt * KS;
@@ -363,16 +521,29 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
       *reinterpret_cast<uint4 *>(lb + off) = rb[j];
     }
   };
+  (void)nfull;
   gload(0);
   lstore(0);
   __syncthreads();
+  if (nk > 1) gload(1);
+  read_frags(0, 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) gload(kt + 1);
-    compute(st);
-    if (more) lstore(st ^ 1);
+    read_frags(1, st, 1);
+    mfmas(0);
+    interleave();
+    read_frags(0, st, 2);
+    mfmas(1);
+    interleave();
+    read_frags(1, st, 3);
+    mfmas(0);
+    interleave();
+    if (kt + 1 < nk) lstore(st ^ 1);
     __syncthreads();
+    if (kt + 2 < nk) gload(kt + 2);
+    if (kt + 1 < nk) read_frags(0, st ^ 1, 0);
+    mfmas(1);
+    interleave();
   }
 #endif
 

@@ -302,12 +302,22 @@ muon_status build_plan(muon_plan *p) {
       W.k1_matrix.push_back(q.matrix);
 
       const int grp = M.ops32 ? PG_F32 : (q.m >= BIG_TILE_MIN_M ? PG_BF16_BIG : PG_BF16);
+      // Tiles of a problem in 4 x 8 blocks (block-row-major, row-major inside
+      // a block): the large-tile kernel hands each XCD 32 consecutive
+      // entries, i.e. one block, whose 12 operand panels its L2 then shares.
       auto add_tiles = [&](int tile, int lmm, int lmn) {
         const int64_t tmn = cdiv(q.m, tile), tnn = cdiv(q.n, tile);
-        for (int64_t a = 0; a < tmn; ++a)
-          for (int64_t b = a; b < tmn; ++b) W.tiles[grp][lmm].push_back(TileDev{(int32_t)li, (int16_t)a, (int16_t)b});
-        for (int64_t a = 0; a < tmn; ++a)
-          for (int64_t b = 0; b < tnn; ++b) W.tiles[grp][lmn].push_back(TileDev{(int32_t)li, (int16_t)a, (int16_t)b});
+        constexpr int64_t BR = 4, BC = 8;
+        for (int64_t A0 = 0; A0 < tmn; A0 += BR)
+          for (int64_t B0 = 0; B0 < tmn; B0 += BC)
+            for (int64_t a = A0; a < std::min(A0 + BR, tmn); ++a)
+              for (int64_t b = std::max(B0, a); b < std::min(B0 + BC, tmn); ++b)
+                W.tiles[grp][lmm].push_back(TileDev{(int32_t)li, (int16_t)a, (int16_t)b});
+        for (int64_t A0 = 0; A0 < tmn; A0 += BR)
+          for (int64_t B0 = 0; B0 < tnn; B0 += BC)
+            for (int64_t a = A0; a < std::min(A0 + BR, tmn); ++a)
+              for (int64_t b = B0; b < std::min(B0 + BC, tnn); ++b)
+                W.tiles[grp][lmn].push_back(TileDev{(int32_t)li, (int16_t)a, (int16_t)b});
       };
       add_tiles(GEMM_TILE, TL_MM128, TL_MN128);
       if (grp == PG_BF16_BIG) add_tiles(BIG_TILE, TL_MM256, TL_MN256);
