@@ -95,6 +95,35 @@ def _views(flat, shapes):
     return out
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ns_gemm_llama7b_32layer_hbm_traffic.md")
+TRAFFIC_SOURCES = ("muon_newton_schulz_step_amd/csrc/k_gemm256.hip", "muon_newton_schulz_step_amd/csrc/k_gemm.hip",
+                   "muon_newton_schulz_step_amd/csrc/plan.cpp")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per Newton-Schulz launch from the committed FETCH_SIZE /
+    WRITE_SIZE summary, or None if it was taken on another workload or the
+    kernel sources changed since."""
+    import hashlib
+    if workload != "llama7b_32layer" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for ln in open(TRAFFIC_FILE):
+        if ":" in ln and not ln.startswith(("|", "#", "`")):
+            k, _, v = ln.partition(":")
+            kv[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if kv.get("kernel_src_sha256_16") != h.hexdigest()[:16]:
+        return None
+    try:
+        return float(kv["ns_gemm_traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(wl, method: str, total_nominal: float, budget_s: float):
     """The oracle (fp64 numpy, as it stands) on a bounded sample: the first
     matrix of the group run through the whole step (momentum, Newton-Schulz,
@@ -153,6 +182,9 @@ def main() -> int:
     ap.add_argument("--precision", default="bf16")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=float, default=0.0,
+                    help="only copy this many GiB device-to-device (a plain copy of known size, the reference "
+                         "for scaling the FETCH_SIZE / WRITE_SIZE counters), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -167,6 +199,15 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.calibrate_copy > 0:
+        n = int(args.calibrate_copy * (1 << 30))
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n}), flush=True)
+        return 0
     M.load()
     wl = W.custom(args.workload) if args.workload.startswith("custom:") else W.ALL[args.workload]()
     method = args.method or wl.methods[0]
@@ -262,7 +303,8 @@ def main() -> int:
         "accumulate_gbs": round(acc_bytes / (statistics.mean(acc_ms) * 1e-3) / 1e9, 1) if acc is not None else None,
         "roofline": {"kernel": "ns_gemm (grouped Newton-Schulz GEMM)", "bound": "mfma",
                      "achieved": round(ns_tflops_sym, 1), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(ns_tflops_sym / peak, 4), "traffic": None,
+                     "frac": round(ns_tflops_sym / peak, 4), "traffic": measured_traffic(wl.name),
+                     "traffic_unit": "bytes per launch (HBM read + write, rocprofv3 FETCH_SIZE/WRITE_SIZE)",
                      "flops_per_step": sym, "launches_per_step": nl,
                      "avg_launch_ms": round(ns_ms / max(nl, 1), 4)},
     }
