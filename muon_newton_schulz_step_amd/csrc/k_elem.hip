@@ -50,6 +50,33 @@ __device__ __forceinline__ int find_owner(int n, int64_t t, F key) {
 
 // ----------------------------------------------------------------- K0
 
+// 8 consecutive elements -> fp32 (16-byte bf16 load or two 16-byte fp32 loads)
+template <bool BF16>
+__device__ __forceinline__ void load8(const void *p, int64_t i, float *v) {
+  if constexpr (BF16) {
+    const uint4 w = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p) + i);
+    const uint32_t x[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = __uint_as_float(x[k] << 16);
+      v[2 * k + 1] = __uint_as_float(x[k] & 0xffff0000u);
+    }
+  } else {
+    const float4 a = *reinterpret_cast<const float4 *>(static_cast<const float *>(p) + i);
+    const float4 b = *reinterpret_cast<const float4 *>(static_cast<const float *>(p) + i + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+__device__ __forceinline__ void store8_f32(float *p, const float *v) {
+  *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4 *>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+__device__ __forceinline__ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Each workgroup owns K0_CHUNK elements of one matrix; 8 per lane per
+// iteration when the chunk is 16-byte aligned on both sides.
 template <bool GBF16>
 __global__ __launch_bounds__(256) void k0_accumulate(const K0Mat *mats, int nmat, int first) {
   const int64_t ch = blockIdx.x;
@@ -58,14 +85,65 @@ __global__ __launch_bounds__(256) void k0_accumulate(const K0Mat *mats, int nmat
   const void *g = mats[i].g;
   const int64_t start = (ch - mats[i].chunk0) * K0_CHUNK;
   const int64_t end = min(start + (int64_t)K0_CHUNK, mats[i].numel);
-  for (int64_t j = start + threadIdx.x; j < end; j += 256) {
-    float v = load_as_f32<GBF16>(g, j);
+  const bool vec = aligned16(acc + start) && aligned16(GBF16 ? (const void *)(static_cast<const uint16_t *>(g) + start)
+                                                             : (const void *)(static_cast<const float *>(g) + start));
+  int64_t j = start;
+  if (vec) {
+    for (j = start + 8 * threadIdx.x; j + 8 <= end; j += 8 * 256) {
+      float v[8];
+      load8<GBF16>(g, j, v);
+      if (!first) {
+        float a[8];
+        load8<false>(acc, j, a);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = a[k] + v[k];
+      }
+      store8_f32(acc + j, v);
+    }
+    j = start + (end - start) / 8 * 8;   // scalar tail
+    for (j += threadIdx.x; j < end; j += 256) {
+      const float v = load_as_f32<GBF16>(g, j);
+      acc[j] = first ? v : acc[j] + v;
+    }
+    return;
+  }
+  for (j = start + threadIdx.x; j < end; j += 256) {
+    const float v = load_as_f32<GBF16>(g, j);
     acc[j] = first ? v : acc[j] + v;
   }
 }
 
 // ----------------------------------------------------------------- K1
 
+// 4 consecutive elements -> fp32 / fp32 -> 4 consecutive elements
+template <bool BF16>
+__device__ __forceinline__ void load4(const void *p, int64_t i, float *v) {
+  if constexpr (BF16) {
+    const uint2 w = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p) + i);
+    v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xffff0000u);
+    v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xffff0000u);
+  } else {
+    const float4 a = *reinterpret_cast<const float4 *>(static_cast<const float *>(p) + i);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  }
+}
+
+__device__ __forceinline__ void store4(void *p, int64_t i, const float *v, bool bf16) {
+  if (bf16) {
+    uint2 w;
+    w.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    w.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p) + i) = w;
+  } else {
+    *reinterpret_cast<float4 *>(static_cast<float *>(p) + i) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+// One 64 x 64 tile of one block per workgroup.  Pass 1: each thread takes
+// row quads (4 consecutive columns) of rows ty, ty+16, ty+32, ty+48; vector
+// loads/stores when the matrix rows are 16-byte aligned and the quad is
+// whole, element accesses otherwise.  Pass 2: the transposed copy, one
+// 4-row quad of one column per access, read from the LDS tile.
 template <bool GBF16>
 __global__ __launch_bounds__(256) void k1_momentum(const K1Prob *probs, int nprob, char *ws, float *partials,
                                                    float beta, float omb, int nesterov) {
@@ -77,41 +155,76 @@ __global__ __launch_bounds__(256) void k1_momentum(const K1Prob *probs, int npro
   const int lt = t - P.tile0;
   const int tr = lt / P.tiles_c, tc = lt - tr * P.tiles_c;
   const int r0 = tr * K1_TILE, c0 = tc * K1_TILE;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   void *orig = ws + P.orig_off;
   void *trans = ws + P.trans_off;
+  const bool xb = P.xbf16 != 0;
+  const bool vec_rows = (P.cols % 4) == 0 && aligned16(P.mom) && ((reinterpret_cast<uintptr_t>(P.grad) & (GBF16 ? 7 : 15)) == 0);
   float ss = 0.f;
-  const int64_t c = c0 + tx;
-  for (int i = 0; i < 16; ++i) {
-    const int r = ty * 16 + i;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int cq = tx * 4;
+  const int64_t c = c0 + cq;
+  auto one = [&](float g, float m, float &mn, float &u) {
+    const float og = omb * g;
+    mn = fmaf(beta, m, og);
+    u = nesterov ? fmaf(beta, mn, og) : mn;
+  };
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = ty + 16 * i;
     const int64_t gr = r0 + r;
-    float u = 0.f;
-    if (gr < P.hr && c < P.cols) {
-      const int64_t idx = (P.row0 + gr) * P.cols + c;
-      const float g = load_as_f32<GBF16>(P.grad, idx);
-      const float m = P.mom[idx];
-      const float og = omb * g;
-      const float mn = fmaf(beta, m, og);
-      P.mom[idx] = mn;
-      u = nesterov ? fmaf(beta, mn, og) : mn;
-      ss = fmaf(u, u, ss);
-      if (P.xbf16) store_from_f32<true>(orig, gr * P.orig_ld + c, u);
-      else store_from_f32<false>(orig, gr * P.orig_ld + c, u);
+    float u[4] = {0.f, 0.f, 0.f, 0.f};
+    if (gr < P.hr) {
+      const int64_t base = (P.row0 + gr) * P.cols;
+      if (vec_rows && c + 3 < P.cols) {
+        float g[4], m[4], mn[4];
+        load4<GBF16>(P.grad, base + c, g);
+        load4<false>(P.mom, base + c, m);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) one(g[e], m[e], mn[e], u[e]);
+        store4(P.mom, base + c, mn, false);
+        store4(orig, gr * P.orig_ld + c, u, xb);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (c + e < P.cols) {
+            float mn;
+            one(load_as_f32<GBF16>(P.grad, base + c + e), P.mom[base + c + e], mn, u[e]);
+            P.mom[base + c + e] = mn;
+            if (xb) store_from_f32<true>(orig, gr * P.orig_ld + c + e, u[e]);
+            else store_from_f32<false>(orig, gr * P.orig_ld + c + e, u[e]);
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ss = fmaf(u[e], u[e], ss);
     }
-    tile[r][tx] = u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tile[r][cq + e] = u[e];
   }
   __syncthreads();
-  for (int i = 0; i < 16; ++i) {
-    const int cc = ty * 16 + i;
-    const int64_t gc = c0 + cc, gr = r0 + tx;
-    if (gc < P.cols && gr < P.hr) {
-      if (P.xbf16) store_from_f32<true>(trans, gc * P.trans_ld + gr, tile[tx][cc]);
-      else store_from_f32<false>(trans, gc * P.trans_ld + gr, tile[tx][cc]);
+  // transposed copy: row (c0 + cc) of the transposed block, elements r0 + 4 rq .. + 3
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int q = threadIdx.x + 256 * k;
+    const int cc = q >> 4, rq = (q & 15) * 4;
+    const int64_t gc = c0 + cc, gr = r0 + rq;
+    if (gc >= P.cols || gr >= P.hr) continue;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = tile[rq + e][cc];
+    if (gr + 3 < P.hr) {
+      store4(trans, gc * P.trans_ld + gr, v, xb);
+    } else {
+      for (int e = 0; e < 4 && gr + e < P.hr; ++e) {
+        if (xb) store_from_f32<true>(trans, gc * P.trans_ld + gr + e, v[e]);
+        else store_from_f32<false>(trans, gc * P.trans_ld + gr + e, v[e]);
+      }
     }
   }
   // block sum of squares: wave butterfly, then the 4 waves in order
   for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
-  if (tx == 0) red[ty] = ss;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = ss;
   __syncthreads();
   if (threadIdx.x == 0) partials[t] = (red[0] + red[1]) + (red[2] + red[3]);
 }
@@ -138,17 +251,38 @@ __global__ __launch_bounds__(256) void kn_finalize(const K1Prob *probs, const fl
 
 // ----------------------------------------------------------------- K3
 
+// One IEEE multiply per element.  8 elements per lane when the chunk's
+// source and destination are 16-byte aligned.
+template <bool SBF16>
+__device__ __forceinline__ void k3_body(const K3Run &R, int64_t start, int64_t end) {
+  const void *src = R.src;
+  const bool vec = aligned16(R.dst + start) &&
+                   aligned16(SBF16 ? (const void *)(static_cast<const uint16_t *>(src) + R.first + start)
+                                   : (const void *)(static_cast<const float *>(src) + R.first + start));
+  if (vec) {
+    int64_t j;
+    for (j = start + 8 * threadIdx.x; j + 8 <= end; j += 8 * 256) {
+      float v[8];
+      load8<SBF16>(src, R.first + j, v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = v[k] * R.scale;
+      store8_f32(R.dst + j, v);
+    }
+    for (j = start + (end - start) / 8 * 8 + threadIdx.x; j < end; j += 256)
+      R.dst[j] = load_as_f32<SBF16>(src, R.first + j) * R.scale;
+    return;
+  }
+  for (int64_t j = start + threadIdx.x; j < end; j += 256) R.dst[j] = load_as_f32<SBF16>(src, R.first + j) * R.scale;
+}
+
 __global__ __launch_bounds__(256) void k3_scatter(const K3Run *runs, int nrun) {
   const int64_t ch = blockIdx.x;
   const int i = find_owner(nrun, ch, [&](int k) { return runs[k].chunk0; });
   const K3Run R = runs[i];
   const int64_t start = (ch - R.chunk0) * K3_CHUNK;
   const int64_t end = min(start + (int64_t)K3_CHUNK, R.length);
-  if (R.src_bf16) {
-    for (int64_t j = start + threadIdx.x; j < end; j += 256) R.dst[j] = load_as_f32<true>(R.src, R.first + j) * R.scale;
-  } else {
-    for (int64_t j = start + threadIdx.x; j < end; j += 256) R.dst[j] = load_as_f32<false>(R.src, R.first + j) * R.scale;
-  }
+  if (R.src_bf16) k3_body<true>(R, start, end);
+  else k3_body<false>(R, start, end);
 }
 
 // ----------------------------------------------------------------- KC
