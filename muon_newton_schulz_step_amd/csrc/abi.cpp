@@ -195,7 +195,7 @@ muon_status muon_step(muon_plan *p, const void *const *grads, float *const *mome
       // ones, then fp32-operand ones
       for (int grp = PG_BF16_BIG; grp >= PG_F32; --grp) {
         if (W.tiles[grp][TL_MN128].empty()) continue;
-        const std::vector<Launch> &sched = p->schedule[grp == PG_F32 ? 0 : 1];
+        const std::vector<Launch> &sched = p->schedule[grp == PG_F32 ? 0 : (grp == PG_BF16 ? 1 : 2)];
         for (const Launch &L : sched) {
           const bool big = grp == PG_BF16_BIG && L.kind == Launch::GEMM_OP;
           const int list = big ? (L.mn ? TL_MN256 : TL_MM256) : (L.mn ? TL_MN128 : TL_MM128);

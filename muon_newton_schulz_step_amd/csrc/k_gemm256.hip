@@ -20,9 +20,10 @@
 //    [32 x, 32 x + 32) of each chunk, so the 32 CUs of an XCD work on one
 //    block and share its operand panels in their L2 (measured L2 hit rate
 //    of the stage loads is otherwise about 50%).
-//  - MUON_BIG_RING (default 0) selects an alternative pipeline with a ring
-//    of 32-deep stages; measured slower on MI355X than the two 64-deep
-//    buffers, kept for study.
+//  - A split product (hi.hi + hi.lo + lo.hi of bf16 hi/lo pairs) runs its
+//    three K segments back to back through the same pipeline and
+//    accumulators: stage kt of the concatenated range reads segment
+//    kt / nk, whose operands sit at fixed byte offsets from segment 0's.
 // Rows beyond M or N are clamped to the last valid row when loading; they
 // only feed outputs that are never stored.
 #include <hip/hip_runtime.h>
@@ -35,12 +36,6 @@
 #endif
 #ifndef MUON_XCD_REMAP
 #define MUON_XCD_REMAP 1
-#endif
-#ifndef MUON_BIG_DMA
-#define MUON_BIG_DMA 1
-#endif
-#ifndef MUON_BIG_RING
-#define MUON_BIG_RING 0
 #endif
 
 namespace muon {
@@ -154,6 +149,16 @@ __device__ __forceinline__ void load_quad(const char *base, int64_t idx, float *
   }
 }
 
+// hi = the bf16 value nearest v, lo = v - hi (then rounded to bf16 when
+// stored): hi + lo carries about 16 significant bits of v
+__device__ __forceinline__ void split4(const float *v, float *hi, float *lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    hi[e] = bf2f(f2bf(v[e]));
+    lo[e] = v[e] - hi[e];
+  }
+}
+
 __device__ __forceinline__ uint4 mask_tail_bf16(uint4 v, int valid) {
   uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -164,12 +169,11 @@ __device__ __forceinline__ uint4 mask_tail_bf16(uint4 v, int valid) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// SPLIT: the recipe may carry K segments, a split D and a split output; the
+// plain instance keeps the single-segment pipeline free of them.
+template <bool SPLIT>
 __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles) {
-#if MUON_BIG_RING * 32768 > 131072
-  __shared__ __attribute__((aligned(1024))) char lds[MUON_BIG_RING * 32768];
-#else
   __shared__ __attribute__((aligned(1024))) char lds[2 * 2 * OPB];
-#endif
 
 #if MUON_XCD_REMAP
   // Workgroup i runs on XCD i % 8.  The tile list is cut into chunks of
@@ -191,6 +195,13 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
   const char *A = args.ws + P.off[R.rA];
   const char *B = args.ws + P.off[R.rB];
   const int64_t lda = P.ld[R.rA], ldb = P.ld[R.rB];
+  // K segments 1, 2 of a split product read (rA2[s-1], rB2[s-1]), which the
+  // planner lays out with the leading dimensions of rA and rB
+  int64_t dA1 = 0, dA2 = 0, dB1 = 0, dB2 = 0;
+  if (SPLIT && R.nseg > 1) {
+    dA1 = P.off[R.rA2[0]] - P.off[R.rA]; dB1 = P.off[R.rB2[0]] - P.off[R.rB];
+    dA2 = P.off[R.rA2[1]] - P.off[R.rA]; dB2 = P.off[R.rB2[1]] - P.off[R.rB];
+  }
   const int64_t m0 = (int64_t)tile.tm * BT, n0 = (int64_t)tile.tn * BT;
 
   const int tid = threadIdx.x;
@@ -201,6 +212,14 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
   // loader geometry: wave w stages rows [64 w, 64 w + 64) of both operands,
   // 8 rows (1 KB) per instruction; lane L covers row 64w + 8j + L/8, LDS
   // chunk position L%8, which holds global chunk swz(row, L%8).
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
   const int lrow = lane >> 3, lpos = lane & 7;
   int64_t arow[8], brow[8];
   int lchunk[8];
@@ -213,45 +232,42 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
   }
   const int nfull = (int)(K / KS);
   const int nk = (int)((K + KS - 1) / KS);
+  const int nkt = SPLIT ? nk * R.nseg : nk;          // stages over all K segments
 
-  auto dma_stage = [&](int kt, int st) {
-    const int64_t k0 = (int64_t)kt * KS;
+  // stage kt of the concatenated range into LDS buffer st: full stages by
+  // LDS-DMA, a ragged one through registers with k >= K zeroed
+  auto stage = [&](int kt, int st) {
+    const int seg = !SPLIT ? 0 : (kt >= nk ? (kt >= 2 * nk ? 2 : 1) : 0);
+    const int kk = kt - seg * nk;
+    const char *a = A + (seg == 0 ? 0 : (seg == 1 ? dA1 : dA2));
+    const char *b = B + (seg == 0 ? 0 : (seg == 1 ? dB1 : dB2));
+    const int64_t k0 = (int64_t)kk * KS;
     char *la = lds + st * 2 * OPB;
     char *lb = la + OPB;
+    if (kk < nfull) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int off = (wave * 64 + j * 8) * ROWB;
-      __builtin_amdgcn_global_load_lds(A + (arow[j] + k0 + lchunk[j]) * 2, (lds_void *)(la + off), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(B + (brow[j] + k0 + lchunk[j]) * 2, (lds_void *)(lb + off), 16, 0, 0);
-    }
-  };
-  auto reg_stage = [&](int kt, int st) {
-    const int64_t k0 = (int64_t)kt * KS;
-    char *la = lds + st * 2 * OPB;
-    char *lb = la + OPB;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t gk = k0 + lchunk[j];
-      const int valid = (int)min<int64_t>(K - gk, 8);
-      uint4 va = make_uint4(0, 0, 0, 0), vb = make_uint4(0, 0, 0, 0);
-      if (valid > 0) {
-        va = *reinterpret_cast<const uint4 *>(A + (arow[j] + gk) * 2);
-        vb = *reinterpret_cast<const uint4 *>(B + (brow[j] + gk) * 2);
-        if (valid < 8) { va = mask_tail_bf16(va, valid); vb = mask_tail_bf16(vb, valid); }
+      for (int j = 0; j < 8; ++j) {
+        const int off = (wave * 64 + j * 8) * ROWB;
+        __builtin_amdgcn_global_load_lds(a + (arow[j] + k0 + lchunk[j]) * 2, (lds_void *)(la + off), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(b + (brow[j] + k0 + lchunk[j]) * 2, (lds_void *)(lb + off), 16, 0, 0);
       }
-      const int off = (wave * 64 + j * 8) * ROWB + lane * 16;
-      *reinterpret_cast<uint4 *>(la + off) = va;
-      *reinterpret_cast<uint4 *>(lb + off) = vb;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int64_t gk = k0 + lchunk[j];
+        const int valid = (int)min<int64_t>(K - gk, 8);
+        uint4 va = make_uint4(0, 0, 0, 0), vb = make_uint4(0, 0, 0, 0);
+        if (valid > 0) {
+          va = *reinterpret_cast<const uint4 *>(a + (arow[j] + gk) * 2);
+          vb = *reinterpret_cast<const uint4 *>(b + (brow[j] + gk) * 2);
+          if (valid < 8) { va = mask_tail_bf16(va, valid); vb = mask_tail_bf16(vb, valid); }
+        }
+        const int off = (wave * 64 + j * 8) * ROWB + lane * 16;
+        *reinterpret_cast<uint4 *>(la + off) = va;
+        *reinterpret_cast<uint4 *>(lb + off) = vb;
+      }
     }
   };
-
-  f32x16_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   // fragment row offsets (bytes) and the per-row swizzle key
   int arb[4], brb[4], ak[4], bk[4];
@@ -280,129 +296,6 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
     }
   };
 
-#if MUON_BIG_RING
-  // Ring of MUON_BIG_RING stages, each 32 deep (64-byte rows, 4 chunks,
-  // position = chunk ^ ((row >> 2) & 3)), filled by LDS-DMA up to RING-1
-  // stages ahead.  Each stage is two 16-deep k-steps; the barrier sits
-  // before the second one.  At the barrier of stage t only the DMA of stage
-  // t+1 must have landed (vmcnt may still count RING-2 later stages).
-  constexpr int RS = 32;                // K elements per ring stage
-  constexpr int RROW = 64;              // bytes per staged row
-  constexpr int ROP = BT * RROW;        // 16 KB per operand per stage
-  constexpr int NB = MUON_BIG_RING;
-  static_assert(NB * 2 * ROP <= (int)sizeof(lds), "ring exceeds the LDS allocation");
-  auto rswz = [](int r, int c) { return c ^ ((r >> 2) & 3); };
-  // loader: wave w stages rows [64 w, 64 w + 64), 16 rows (1 KB) per
-  // instruction; lane L covers row 64w + 16j + L/4, position L%4
-  int64_t rar[4], rbr[4];
-  int rch[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = wave * 64 + j * 16 + (lane >> 2);
-    rar[j] = min(m0 + r, M - 1) * lda;
-    rbr[j] = min(n0 + r, N - 1) * ldb;
-    rch[j] = rswz(r, lane & 3) * 8;
-  }
-  const int rnfull = (int)(K / RS);
-  const int rnk = (int)((K + RS - 1) / RS);
-  // half h (0/1) of stage kt: A and B rows j = 2h, 2h+1 of this wave
-  // (4 DMA instructions); a ragged stage is staged whole, through
-  // registers, by its first half
-  auto ring_half = [&](int kt, int h) {
-    const int64_t k0 = (int64_t)kt * RS;
-    char *la = lds + (kt % NB) * 2 * ROP;
-    char *lb = la + ROP;
-    if (kt < rnfull) {
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int j = 2 * h + jj;
-        const int off = (wave * 64 + j * 16) * RROW;
-        __builtin_amdgcn_global_load_lds(A + (rar[j] + k0 + rch[j]) * 2, (lds_void *)(la + off), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(B + (rbr[j] + k0 + rch[j]) * 2, (lds_void *)(lb + off), 16, 0, 0);
-      }
-    } else if (h == 0) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t gk = k0 + rch[j];
-        const int valid = (int)min<int64_t>(K - gk, 8);
-        uint4 va = make_uint4(0, 0, 0, 0), vb = make_uint4(0, 0, 0, 0);
-        if (valid > 0) {
-          va = *reinterpret_cast<const uint4 *>(A + (rar[j] + gk) * 2);
-          vb = *reinterpret_cast<const uint4 *>(B + (rbr[j] + gk) * 2);
-          if (valid < 8) { va = mask_tail_bf16(va, valid); vb = mask_tail_bf16(vb, valid); }
-        }
-        const int off = (wave * 64 + j * 16) * RROW + lane * 16;
-        *reinterpret_cast<uint4 *>(la + off) = va;
-        *reinterpret_cast<uint4 *>(lb + off) = vb;
-      }
-    }
-  };
-  int rab[4], rbb[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    rab[i] = (wm * 128 + i * 32 + lr) * RROW;
-    rbb[i] = (wn * 128 + i * 32 + lr) * RROW;
-  }
-  bf16x8_t fa[2][4], fb[2][4];
-  auto read_frags = [&](int set, int kt, int ks) {
-    const char *la = lds + (kt % NB) * 2 * ROP;
-    const char *lb = la + ROP;
-    const int c = ks * 2 + lg;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fa[set][i] = *reinterpret_cast<const bf16x8_t *>(la + rab[i] + rswz(ak[i], c) * 16);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) fb[set][j] = *reinterpret_cast<const bf16x8_t *>(lb + rbb[j] + rswz(bk[j], c) * 16);
-  };
-  auto mfmas = [&](int set) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
-  };
-  // 16 MFMAs with the 8 fragment reads of the next k-step and the 4 DMA
-  // instructions of half a stage spread between them
-  auto interleave = [&]() {
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-  };
-  (void)nfull; (void)nk;
-  for (int t = 0; t < NB - 1 && t < rnk; ++t) { ring_half(t, 0); ring_half(t, 1); }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // prologue: keep it simple
-  __syncthreads();
-  read_frags(0, 0, 0);
-  for (int kt = 0; kt < rnk; ++kt) {
-    // stage kt+NB-1 goes into the buffer of stage kt-1, free since the
-    // barrier of stage kt-1; its two halves are issued across this stage
-    const int sn = kt + NB - 1;
-    read_frags(1, kt, 1);
-    if (sn < rnk) ring_half(sn, 0);
-    mfmas(0);
-    interleave();
-    // Issued so far: stages <= kt+NB-2 and half of stage kt+NB-1.  Stage
-    // kt+1 must have landed; stages kt+2 .. kt+NB-2 (8 DMA instructions
-    // each) and the first half of kt+NB-1 (4) may be in flight.  Loads
-    // complete in issue order for vmcnt.
-    if (sn < rnfull) {
-      if constexpr (NB == 5) asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
-      else if constexpr (NB == 4) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    __syncthreads();
-    if (sn < rnk) ring_half(sn, 1);
-    if (kt + 1 < rnk) read_frags(0, kt + 1, 0);
-    mfmas(1);
-    interleave();
-  }
-#elif MUON_BIG_DMA
   // Software pipeline over 16-deep k-steps: the fragments of step s+1 are
   // read from LDS while the 16 MFMAs of step s run (two fragment sets).
   // The stage barrier sits before the last k-step of each stage, so the
@@ -433,16 +326,12 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
-  if (nfull > 0) dma_stage(0, 0);
-  else reg_stage(0, 0);
+  stage(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (nk > 1) {
-    if (1 < nfull) dma_stage(1, 1);
-    else reg_stage(1, 1);
-  }
+  if (nkt > 1) stage(1, 1);
   read_frags(0, 0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
+  for (int kt = 0; kt < nkt; ++kt) {
     const int st = kt & 1;
     // k-steps 0..2: MFMAs of step s, reads of step s+1 (same stage)
     read_frags(1, st, 1);
@@ -458,94 +347,11 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
     // refill buffer st with stage t+2 and start reading stage t+1
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (kt + 2 < nk) {
-      if (kt + 2 < nfull) dma_stage(kt + 2, st);
-      else reg_stage(kt + 2, st);
-    }
-    if (kt + 1 < nk) read_frags(0, st ^ 1, 0);
+    if (kt + 2 < nkt) stage(kt + 2, st);
+    if (kt + 1 < nkt) read_frags(0, st ^ 1, 0);
     mfmas(1);
     interleave();
   }
-#else
-  // Register-staged variant of the same pipeline: the global loads of stage
-  // t+2 are issued into VGPRs right after the barrier of stage t and written
-  // to the free LDS buffer just before the next barrier.
-  bf16x8_t fa[2][4], fb[2][4];
-  auto read_frags = [&](int set, int st, int ks) {
-    const char *la = lds + st * 2 * OPB;
-    const char *lb = la + OPB;
-    const int c = ks * 2 + lg;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fa[set][i] = *reinterpret_cast<const bf16x8_t *>(la + arb[i] + swz(ak[i], c) * 16);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) fb[set][j] = *reinterpret_cast<const bf16x8_t *>(lb + brb[j] + swz(bk[j], c) * 16);
-  };
-  auto mfmas = [&](int set) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
-  };
-  auto interleave = [&]() {
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-  };
-  uint4 ra[8], rb[8];
-  auto gload = [&](int kt) {
-    const int64_t k0 = (int64_t)kt * KS;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t gk = k0 + lchunk[j];
-      const int valid = (int)min<int64_t>(K - gk, 8);
-      uint4 va = make_uint4(0, 0, 0, 0), vb = make_uint4(0, 0, 0, 0);
-      if (valid > 0) {
-        va = *reinterpret_cast<const uint4 *>(A + (arow[j] + gk) * 2);
-        vb = *reinterpret_cast<const uint4 *>(B + (brow[j] + gk) * 2);
-        if (valid < 8) { va = mask_tail_bf16(va, valid); vb = mask_tail_bf16(vb, valid); }
-      }
-      ra[j] = va;
-      rb[j] = vb;
-    }
-  };
-  auto lstore = [&](int st) {
-    char *la = lds + st * 2 * OPB;
-    char *lb = la + OPB;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int off = (wave * 64 + j * 8) * ROWB + lane * 16;
-      *reinterpret_cast<uint4 *>(la + off) = ra[j];
-      *reinterpret_cast<uint4 *>(lb + off) = rb[j];
-    }
-  };
-  (void)nfull;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  if (nk > 1) gload(1);
-  read_frags(0, 0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    read_frags(1, st, 1);
-    mfmas(0);
-    interleave();
-    read_frags(0, st, 2);
-    mfmas(1);
-    interleave();
-    read_frags(1, st, 3);
-    mfmas(0);
-    interleave();
-    if (kt + 1 < nk) lstore(st ^ 1);
-    __syncthreads();
-    if (kt + 2 < nk) gload(kt + 2);
-    if (kt + 1 < nk) read_frags(0, st ^ 1, 0);
-    mfmas(1);
-    interleave();
-  }
-#endif
 
   // ---- epilogue: C = s^p (cd D + cacc acc) + cdiag I, stored to S0/S1.
   // The tile leaves registers in four passes of 64 rows (block row p of
@@ -573,6 +379,9 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
   const bool diag = (R.flags & GF_DIAG) != 0;
   const char *D = R.rD >= 0 ? args.ws + P.off[R.rD] : nullptr;
   const int64_t ldd = R.rD >= 0 ? P.ld[R.rD] : 0;
+  const bool dsplit = SPLIT && (R.flags & GF_D_SPLIT) != 0;
+  const char *D2 = dsplit ? args.ws + P.off[R.rD2] : nullptr;
+  const bool osplit = SPLIT && (R.flags & GF_SPLIT_OUT) != 0;
   char *S0 = args.ws + P.off[R.rS0];
   const int64_t ld0 = P.ld[R.rS0];
   char *S1 = R.rS1 >= 0 ? args.ws + P.off[R.rS1] : nullptr;
@@ -608,6 +417,12 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
         const int nv = (int)min<int64_t>(N - gj, 4);
         float dv[4] = {0.f, 0.f, 0.f, 0.f};
         if (D && nv > 0) load_quad(D, gi * ldd + gj, dv, nv, fd);
+        if (dsplit && nv > 0) {
+          float dl[4] = {0.f, 0.f, 0.f, 0.f};
+          load_quad(D2, gi * ldd + gj, dl, nv, false);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dv[e] += dl[e];
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float x = v[e];
@@ -618,8 +433,14 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
         }
         if (col_phase) *reinterpret_cast<float4 *>(src) = make_float4(v[0], v[1], v[2], v[3]);
         if (nv > 0) {
-          if (!t0) store_quad(S0, gi * ld0 + gj, v, nv, f0);
-          if (S1 && !t1) store_quad(S1, gi * ld1 + gj, v, nv, f1);
+          if (osplit) {
+            float hi[4], lo[4];
+            split4(v, hi, lo);
+            if (!t0) { store_quad(S0, gi * ld0 + gj, hi, nv, false); store_quad(S1, gi * ld1 + gj, lo, nv, false); }
+          } else {
+            if (!t0) store_quad(S0, gi * ld0 + gj, v, nv, f0);
+            if (S1 && !t1) store_quad(S1, gi * ld1 + gj, v, nv, f1);
+          }
         }
       }
     }
@@ -637,8 +458,15 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = stg[(r8 + e) * SLD + c];
-        if (t0 || mirror) store_chunk(S0, gj * ld0 + gi, v, nv, f0);
-        if (S1 && (t1 || mirror)) store_chunk(S1, gj * ld1 + gi, v, nv, f1);
+        if (osplit) {
+          float hi[8], lo[8];
+          split4(v, hi, lo);
+          split4(v + 4, hi + 4, lo + 4);
+          if (t0 || mirror) { store_chunk(S0, gj * ld0 + gi, hi, nv, false); store_chunk(S1, gj * ld1 + gi, lo, nv, false); }
+        } else {
+          if (t0 || mirror) store_chunk(S0, gj * ld0 + gi, v, nv, f0);
+          if (S1 && (t1 || mirror)) store_chunk(S1, gj * ld1 + gi, v, nv, f1);
+        }
       }
     }
   }
@@ -648,13 +476,15 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
 
 hipError_t launch_gemm256(const GemmArgs &a, int ntiles, hipStream_t s) {
   if (ntiles <= 0) return hipSuccess;
+  const bool split = a.r.nseg > 1 || (a.r.flags & (GF_SPLIT_OUT | GF_D_SPLIT)) != 0;
+  auto kern = split ? ns_gemm256<true> : ns_gemm256<false>;
 #if MUON_XCD_REMAP
   const int chunk = NXCD * XCD_CUS;
   const int grid = (ntiles + chunk - 1) / chunk * chunk;
-  hipLaunchKernelGGL(ns_gemm256, dim3(grid), dim3(NTHR), 0, s, a, ntiles);
 #else
-  hipLaunchKernelGGL(ns_gemm256, dim3(ntiles), dim3(NTHR), 0, s, a, ntiles);
+  const int grid = ntiles;
 #endif
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(NTHR), 0, s, a, ntiles);
   return hipGetLastError();
 }
 

@@ -56,6 +56,77 @@ static std::vector<muon_run> make_runs(int32_t mi, int64_t off, int64_t numel, i
   return runs;
 }
 
+// Gram form with a split-bf16 m x m chain (large bf16 blocks): every chain
+// matrix is a pair hi = bf16(v), lo = bf16(v - hi), and every chain product
+// X Y^T is hi_X hi_Y^T + hi_X lo_Y^T + lo_X hi_Y^T (three K segments of the
+// bf16 kernel, fp32 accumulation), about 16 significant bits per entry.
+static std::vector<Launch> build_split_gram_schedule(const muon_options &o) {
+  const int T = o.ns_steps;
+  std::vector<Launch> S;
+  auto base = [&](int rS0, int rS1, int flags, float cd, float cacc, float cdiag) {
+    GemmRecipe r;
+    std::memset(&r, 0, sizeof(r));
+    r.rA = r.rB = r.rD = -1; r.rS0 = (int8_t)rS0; r.rS1 = (int8_t)rS1;
+    r.flags = flags; r.cd = cd; r.cacc = cacc; r.cdiag = cdiag;
+    r.nseg = 1; r.rA2[0] = r.rA2[1] = r.rB2[0] = r.rB2[1] = -1; r.rD2 = -1;
+    return r;
+  };
+  auto lo_of = [](int hi) {
+    switch (hi) {
+      case R_MA: return (int)R_MA_LO;
+      case R_MB: return (int)R_MB_LO;
+      case R_Q0: return (int)R_Q0_LO;
+      case R_Q1: return (int)R_Q1_LO;
+      default: return (int)R_MT_LO;
+    }
+  };
+  // product X Y^T of two split matrices (hi roles given)
+  auto split = [&](GemmRecipe r, int X, int Y) {
+    r.rA = (int8_t)X; r.rB = (int8_t)Y;
+    r.nseg = 3;
+    r.rA2[0] = (int8_t)X; r.rB2[0] = (int8_t)lo_of(Y);
+    r.rA2[1] = (int8_t)lo_of(X); r.rB2[1] = (int8_t)Y;
+    return r;
+  };
+  if (T == 0) {
+    S.push_back(Launch{Launch::COPY_SCALED, base(-1, -1, 0, 0.f, 0.f, 0.f), false});
+    return S;
+  }
+  const int SP = GF_SYM | GF_SPLIT_OUT;
+  // R = s^2 X0 X0^T, stored split
+  {
+    GemmRecipe r = base(R_MA, R_MA_LO, SP, 0.f, 1.f, 0.f);
+    r.rA = r.rB = R_XR0; r.dimK = 1; r.scale_pow = 2;
+    S.push_back(Launch{Launch::GEMM_OP, r, false});
+  }
+  int qcur = -1;
+  for (int k = 1; k <= T; ++k) {
+    const bool last = (k == T);
+    // P = a I + b R + c R R; the first P is Q itself
+    const int Pr = (k == 1) ? R_Q0 : R_MB;
+    GemmRecipe rp = split(base(Pr, lo_of(Pr), SP | GF_DIAG | GF_D_SPLIT, o.b, o.c, o.a), R_MA, R_MA);
+    rp.rD = R_MA; rp.rD2 = R_MA_LO;
+    S.push_back(Launch{Launch::GEMM_OP, rp, false});
+    if (k == 1) qcur = R_Q0;
+    else {
+      const int qn = (qcur == R_Q0) ? R_Q1 : R_Q0;
+      S.push_back(Launch{Launch::GEMM_OP, split(base(qn, lo_of(qn), SP, 0.f, 1.f, 0.f), Pr, qcur), false});
+      qcur = qn;
+    }
+    if (!last) {
+      S.push_back(Launch{Launch::GEMM_OP, split(base(R_MT, R_MT_LO, SP, 0.f, 1.f, 0.f), Pr, R_MA), false});
+      S.push_back(Launch{Launch::GEMM_OP, split(base(R_MA, R_MA_LO, SP, 0.f, 1.f, 0.f), R_MT, Pr), false});
+    }
+  }
+  // Y = s Q X0 with the bf16 high half of Q
+  {
+    GemmRecipe r = base(R_U, -1, GF_S0_PROBT, 0.f, 1.f, 0.f);
+    r.rA = (int8_t)qcur; r.rB = R_XC0; r.dimN = 1; r.scale_pow = 1;
+    S.push_back(Launch{Launch::GEMM_OP, r, true});
+  }
+  return S;
+}
+
 // Launch schedule of one operand class (bf16 = bf16 MFMA operands on the
 // m x n side; the Gram form's m x m chain is fp32 in both classes).
 static std::vector<Launch> build_schedule(const muon_options &o, bool bf16) {
@@ -64,13 +135,15 @@ static std::vector<Launch> build_schedule(const muon_options &o, bool bf16) {
   auto recipe = [](int rA, int rB, int rD, int rS0, int rS1, int dM, int dN, int dK, int flags,
                    float cd, float cacc, float cdiag, int sp) {
     GemmRecipe r;
+    std::memset(&r, 0, sizeof(r));
     r.rA = (int8_t)rA; r.rB = (int8_t)rB; r.rD = (int8_t)rD; r.rS0 = (int8_t)rS0; r.rS1 = (int8_t)rS1;
     r.dimM = (int8_t)dM; r.dimN = (int8_t)dN; r.dimK = (int8_t)dK;
     r.flags = flags; r.cd = cd; r.cacc = cacc; r.cdiag = cdiag; r.scale_pow = sp;
+    r.nseg = 1; r.rA2[0] = r.rA2[1] = r.rB2[0] = r.rB2[1] = -1; r.rD2 = -1;
     return r;
   };
   if (T == 0) {
-    S.push_back(Launch{Launch::COPY_SCALED, GemmRecipe{}, false});
+    S.push_back(Launch{Launch::COPY_SCALED, recipe(-1, -1, -1, -1, -1, 0, 0, 0, 0, 0.f, 0.f, 0.f, 0), false});
     return S;
   }
   const int opf32 = bf16 ? 0 : (GF_S0_F32 | GF_S1_F32);
@@ -170,6 +243,7 @@ muon_status build_plan(muon_plan *p) {
       q.ldm = rup(q.m, 8);
       q.flops = nominal_flops(o.method, o.ns_steps, q.m, q.n);
       std::fill(q.mm_off, q.mm_off + 6, -1);
+      std::fill(q.lo_off, q.lo_off + 5, -1);
       p->probs.push_back(q);
     }
   }
@@ -180,10 +254,14 @@ muon_status build_plan(muon_plan *p) {
     int64_t trans = rup(M.heads * M.desc.cols * M.ldhr * M.elem, kAlign);
     return 2 * orig + (standard ? 2 : 1) * trans;
   };
+  auto split_chain = [&](const ProblemPlan &q) {
+    return !standard && !p->mats[q.matrix].ops32 && q.m >= BIG_TILE_MIN_M;
+  };
   auto problem_bytes = [&](const ProblemPlan &q) {
     const int64_t e = p->mats[q.matrix].elem;
     int64_t mm = q.m * q.ldm;
     if (standard) return 2 * rup(mm * e, kAlign);
+    if (split_chain(q)) return 10 * rup(mm * 2, kAlign);
     return 5 * rup(mm * 4, kAlign) + (e == 2 ? rup(mm * 2, kAlign) : 0);
   };
 
@@ -208,6 +286,7 @@ muon_status build_plan(muon_plan *p) {
 
   p->schedule[0] = build_schedule(o, false);
   p->schedule[1] = build_schedule(o, true);
+  p->schedule[2] = standard ? p->schedule[1] : build_split_gram_schedule(o);
 
   int64_t max_k1 = 0, max_probs = 0, max_data = 0;
   for (size_t w = 0; w < p->waves.size(); ++w) {
@@ -226,9 +305,14 @@ muon_status build_plan(muon_plan *p) {
       for (int32_t h = 0; h < M.heads; ++h) {
         ProblemPlan &q = p->probs[M.prob0 + h];
         int64_t mm = q.m * q.ldm;
+        std::fill(q.lo_off, q.lo_off + 5, -1);
         if (standard) {
           q.mm_off[0] = dat.take(mm * e);
           q.mm_off[1] = dat.take(mm * e);
+        } else if (split_chain(q)) {
+          for (int r = 0; r < 5; ++r) q.mm_off[r] = dat.take(mm * 2);
+          for (int r = 0; r < 5; ++r) q.lo_off[r] = dat.take(mm * 2);
+          q.mm_off[5] = -1;
         } else {
           for (int r = 0; r < 5; ++r) q.mm_off[r] = dat.take(mm * 4);
           q.mm_off[5] = e == 2 ? dat.take(mm * 2) : -1;
@@ -275,6 +359,10 @@ muon_status build_plan(muon_plan *p) {
       for (int r = 0; r < 6; ++r) {
         d.off[R_MA + r] = q.mm_off[r];
         d.ld[R_MA + r] = (int32_t)q.ldm;
+      }
+      for (int r = 0; r < 5; ++r) {
+        d.off[R_MA_LO + r] = q.lo_off[r];
+        d.ld[R_MA_LO + r] = (int32_t)q.ldm;
       }
       // U: dense original orientation.  It aliases the original-layout copy
       // of X that the last Newton-Schulz launch does not read: parity T&1 of

@@ -37,6 +37,7 @@ struct ProblemPlan {
   double flops;
   int64_t ldm;
   int64_t mm_off[6];  // R_MA .. R_QB relative to the data base; -1 unused
+  int64_t lo_off[5];  // R_MA_LO .. R_MT_LO (split-bf16 Gram chain); -1 unused
 };
 
 struct WavePlan {
@@ -72,7 +73,9 @@ struct muon_plan {
   std::vector<muon::MatrixPlan> mats;
   std::vector<muon::ProblemPlan> probs;
   std::vector<muon::WavePlan> waves;
-  std::vector<muon::Launch> schedule[2];  // per operand class: [0] fp32, [1] bf16
+  // launch schedules: [0] fp32 operands, [1] bf16 operands, [2] bf16 large
+  // blocks (the split-bf16 Gram chain; equal to [1] for the standard form)
+  std::vector<muon::Launch> schedule[3];
   int64_t tables_bytes = 0;  // all waves' tables, at the head of the workspace
   int64_t partials_off = 0, scales_off = 0, data_off = 0, ws_bytes = 0;
   int64_t max_k1_tiles = 0, max_probs = 0;

@@ -21,6 +21,9 @@ enum Role : int {
   R_MT,       // gram: P R                              [fp32]
   R_QB,       // gram: Q in the operand dtype           [operand dtype]
   R_U,        // unscaled output, original orientation, dense per matrix
+  // split-bf16 Gram chain (large blocks): the low halves of R, P, Q0, Q1, T;
+  // the high halves live in R_MA, R_MB, R_Q0, R_Q1, R_MT as bf16
+  R_MA_LO, R_MB_LO, R_Q0_LO, R_Q1_LO, R_MT_LO,
   NROLES
 };
 
@@ -109,6 +112,12 @@ struct GemmRecipe {
   int32_t flags;                // GF_* bits
   float cd, cacc, cdiag;
   int32_t scale_pow;            // 0, 1 or 2: power of the per-problem norm scale
+  // Extra K segments summed into the same accumulators (split products):
+  // segment s >= 1 multiplies roles (rA2[s-1], rB2[s-1]) over the same K.
+  int8_t nseg;                  // 1 or 3
+  int8_t rA2[2], rB2[2];
+  int8_t rD2;                   // low half of D when GF_D_SPLIT
+  int8_t pad_[2];
 };
 constexpr int32_t GF_SYM = 1;        // output symmetric; tiles list tm <= tn, mirror written
 constexpr int32_t GF_D_F32 = 2;      // D is fp32 (else operand dtype)
@@ -118,5 +127,7 @@ constexpr int32_t GF_S0_TRANS = 16;  // S0 stored transposed
 constexpr int32_t GF_S1_TRANS = 32;  // S1 stored transposed
 constexpr int32_t GF_S0_PROBT = 64;  // S0 transposed iff the problem has PF_TALL
 constexpr int32_t GF_DIAG = 128;     // add cdiag on the diagonal
+constexpr int32_t GF_SPLIT_OUT = 256;  // S0 = bf16(v), S1 = bf16(v - S0): a hi/lo pair
+constexpr int32_t GF_D_SPLIT = 512;    // D = bf16 hi (rD) + bf16 lo (rD2)
 
 }  // namespace muon
