@@ -28,6 +28,8 @@
 // only feed outputs that are never stored.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "elem.hpp"
 #include "tables.hpp"
 
@@ -147,6 +149,24 @@ __device__ __forceinline__ void load_quad(const char *base, int64_t idx, float *
       for (int e = 0; e < n; ++e) v[e] = bf2f(p[e]);
     }
   }
+}
+
+// 8 bf16 <-> floats, 16-byte aligned
+__device__ __forceinline__ void unpack8(const uint4 w, float *v) {
+  const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    v[2 * d] = __uint_as_float(a[d] << 16);
+    v[2 * d + 1] = __uint_as_float(a[d] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ uint4 pack8(const float *v) {
+  uint4 w;
+  w.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+  w.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+  w.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
+  w.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+  return w;
 }
 
 // hi = the bf16 value nearest v, lo = v - hi (then rounded to bf16 when
@@ -387,6 +407,12 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
   char *S1 = R.rS1 >= 0 ? args.ws + P.off[R.rS1] : nullptr;
   const int64_t ld1 = R.rS1 >= 0 ? P.ld[R.rS1] : 0;
   const bool col_phase = t0 || (S1 && t1) || mirror;
+  // Interior tile with bf16 operands and 16-byte aligned rows: the row phase
+  // takes 8-column chunks with the D chunks of a pass loaded up front, so no
+  // wait on the vector-memory counter (which also counts stores) falls
+  // between its stores.
+  const bool fast = m0 + BT <= M && n0 + BT <= N && !f0 && !f1 && !fd && (ld0 & 7) == 0 &&
+                    (!S1 || (ld1 & 7) == 0) && (!D || (ldd & 7) == 0);
 
   auto put = [&](const f32x16_t &blk, int j) {
 #pragma unroll
@@ -398,12 +424,89 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
 #pragma unroll 1
   for (int p = 0; p < 4; ++p) {
     if (p) __syncthreads();
+    // staging row r (0..63) is tile row (r / 32) * 128 + p * 32 + r % 32;
+    // fast row phase: chunk q of thread tid is row (tid + 256 q) / 32,
+    // columns 8 ((tid + 256 q) % 32) .. +8
+    uint4 dq[8], dq2[8];
+    if (fast && D) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int ch = tid + NTHR * q;
+        const int r = ch >> 5, c8 = (ch & 31) * 8;
+        const int64_t gi = m0 + (r >> 5) * 128 + p * 32 + (r & 31);
+        const int64_t e = gi * ldd + n0 + c8;
+        dq[q] = *reinterpret_cast<const uint4 *>(D + e * 2);
+        if (dsplit) dq2[q] = *reinterpret_cast<const uint4 *>(D2 + e * 2);
+      }
+    }
     if (p == 0) { put(acc[0][0], 0); put(acc[0][1], 1); put(acc[0][2], 2); put(acc[0][3], 3); }
     if (p == 1) { put(acc[1][0], 0); put(acc[1][1], 1); put(acc[1][2], 2); put(acc[1][3], 3); }
     if (p == 2) { put(acc[2][0], 0); put(acc[2][1], 1); put(acc[2][2], 2); put(acc[2][3], 3); }
     if (p == 3) { put(acc[3][0], 0); put(acc[3][1], 1); put(acc[3][2], 2); put(acc[3][3], 3); }
     __syncthreads();
-    // staging row r (0..63) is tile row (r / 32) * 128 + p * 32 + r % 32
+    // fast row phase; HAS_D: D chunks in dq (and dq2 when split)
+    auto row_fast = [&](auto has_d) {
+      constexpr bool HAS_D = decltype(has_d)::value;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int ch = tid + NTHR * q;
+        const int r = ch >> 5, c8 = (ch & 31) * 8;
+        const int64_t gi = m0 + (r >> 5) * 128 + p * 32 + (r & 31);
+        const int64_t gj = n0 + c8;
+        float *src = stg + r * SLD + c8;
+        const float4 a4 = *reinterpret_cast<const float4 *>(src);
+        const float4 b4 = *reinterpret_cast<const float4 *>(src + 4);
+        float v[8] = {a4.x, a4.y, a4.z, a4.w, b4.x, b4.y, b4.z, b4.w};
+        if constexpr (HAS_D) {
+          float dv[8];
+          unpack8(dq[q], dv);
+          if (dsplit) {
+            float dl[8];
+            unpack8(dq2[q], dl);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dv[e] += dl[e];
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = fmaf(R.cd, dv[e], v[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] *= sc;
+        if (diag) {
+          const int64_t dd = gi - gj;
+          if (dd >= 0 && dd < 8) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (e == dd) v[e] += R.cdiag;
+          }
+        }
+        if (col_phase) {
+          *reinterpret_cast<float4 *>(src) = make_float4(v[0], v[1], v[2], v[3]);
+          *reinterpret_cast<float4 *>(src + 4) = make_float4(v[4], v[5], v[6], v[7]);
+        }
+        if (osplit) {
+          float hi[8], lo[8];
+          split4(v, hi, lo);
+          split4(v + 4, hi + 4, lo + 4);
+          if (!t0) {
+            *reinterpret_cast<uint4 *>(S0 + (gi * ld0 + gj) * 2) = pack8(hi);
+            *reinterpret_cast<uint4 *>(S1 + (gi * ld1 + gj) * 2) = pack8(lo);
+          }
+        } else {
+          if (!t0) *reinterpret_cast<uint4 *>(S0 + (gi * ld0 + gj) * 2) = pack8(v);
+          if (S1 && !t1) *reinterpret_cast<uint4 *>(S1 + (gi * ld1 + gj) * 2) = pack8(v);
+        }
+      }
+    };
+    if (fast) {
+      if (D) {
+        // every D chunk of the pass has landed (this also waits for the
+        // previous pass's stores); no store of this pass waits on anything
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        row_fast(std::true_type{});
+      } else {
+        row_fast(std::false_type{});
+      }
+    } else {
 #pragma unroll 1
     for (int q = 0; q < 16; ++q) {
       const int ch = tid + NTHR * q;        // 4096 quads: 64 rows x 64 quads
@@ -443,6 +546,7 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
           }
         }
       }
+    }
     }
     if (col_phase) {
       __syncthreads();
