@@ -297,25 +297,6 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
     arb[i] = ra_ * ROWB; ak[i] = ra_;
     brb[i] = rb_ * ROWB; bk[i] = rb_;
   }
-  auto compute = [&](int st) {
-    const char *la = lds + st * 2 * OPB;
-    const char *lb = la + OPB;
-#pragma unroll
-    for (int ks = 0; ks < KS / 16; ++ks) {
-      const int c = ks * 2 + lg;
-      bf16x8_t a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8_t *>(la + arb[i] + swz(ak[i], c) * 16);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const bf16x8_t *>(lb + brb[j] + swz(bk[j], c) * 16);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-  };
-
   // Software pipeline over 16-deep k-steps: the fragments of step s+1 are
   // read from LDS while the 16 MFMAs of step s run (two fragment sets).
   // The stage barrier sits before the last k-step of each stage, so the
@@ -346,6 +327,76 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
+  if (nfull == nk) {
+    // K a multiple of 64: every stage is a whole LDS-DMA stage, issued
+    // without branches so that its 16 instructions interleave with the
+    // MFMAs of the step that follows the barrier.  The destination rows of
+    // this wave are uniform, so M0 is computed on the scalar unit.
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    auto dma = [&](int kt, int st) {
+      const int seg = !SPLIT ? 0 : (kt >= nk ? (kt >= 2 * nk ? 2 : 1) : 0);
+      const int64_t k0 = (int64_t)(kt - seg * nk) * KS;
+      const char *a = A + (seg == 0 ? 0 : (seg == 1 ? dA1 : dA2));
+      const char *b = B + (seg == 0 ? 0 : (seg == 1 ? dB1 : dB2));
+      char *la = lds + st * 2 * OPB + wv * 64 * ROWB;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        __builtin_amdgcn_global_load_lds(a + (arow[j] + k0 + lchunk[j]) * 2, (lds_void *)(la + j * 8 * ROWB), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(b + (brow[j] + k0 + lchunk[j]) * 2, (lds_void *)(la + OPB + j * 8 * ROWB), 16,
+                                         0, 0);
+      }
+    };
+    auto interleave_dma = [&]() {
+      // 16 MFMAs with the 16 LDS-DMA instructions and 8 fragment reads
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x010, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    };
+    dma(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (nkt > 1) dma(1, 1);
+    read_frags(0, 0, 0);
+    int kt = 0;
+    for (; kt + 2 < nkt; ++kt) {
+      const int st = kt & 1;
+      read_frags(1, st, 1);
+      mfmas(0);
+      interleave();
+      read_frags(0, st, 2);
+      mfmas(1);
+      interleave();
+      read_frags(1, st, 3);
+      mfmas(0);
+      interleave();
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      dma(kt + 2, st);
+      read_frags(0, st ^ 1, 0);
+      mfmas(1);
+      interleave_dma();
+    }
+    for (; kt < nkt; ++kt) {            // the last two stages: nothing left to load
+      const int st = kt & 1;
+      read_frags(1, st, 1);
+      mfmas(0);
+      interleave();
+      read_frags(0, st, 2);
+      mfmas(1);
+      interleave();
+      read_frags(1, st, 3);
+      mfmas(0);
+      interleave();
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (kt + 1 < nkt) read_frags(0, st ^ 1, 0);
+      mfmas(1);
+      interleave();
+    }
+  } else {
   stage(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -371,6 +422,7 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
     if (kt + 1 < nkt) read_frags(0, st ^ 1, 0);
     mfmas(1);
     interleave();
+  }
   }
 
   // ---- epilogue: C = s^p (cd D + cacc acc) + cdiag I, stored to S0/S1.
@@ -414,11 +466,17 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
   const bool fast = m0 + BT <= M && n0 + BT <= N && !f0 && !f1 && !fd && (ld0 & 7) == 0 &&
                     (!S1 || (ld1 & 7) == 0) && (!D || (ldd & 7) == 0);
 
+  // Staged row r (0..63) = 8-row group g = r / 8, element e = r % 8 lives in
+  // LDS row 8 g + (e + 2 (g % 4)) % 8: the column gather of the transposed
+  // stores (rows 8 k + e of one column for k = 0..3 across lanes) then hits
+  // 64 distinct banks, and the two half-waves of an accumulator write still
+  // land 32 banks apart.
+  auto srow = [](int r) { return (r & ~7) | ((r + ((r >> 3) & 3) * 2) & 7); };
   auto put = [&](const f32x16_t &blk, int j) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int r = wm * 32 + 8 * (v >> 2) + 4 * lg + (v & 3);
-      stg[r * SLD + wn * 128 + j * 32 + lr] = blk[v] * R.cacc;
+      stg[srow(r) * SLD + wn * 128 + j * 32 + lr] = blk[v] * R.cacc;
     }
   };
 #pragma unroll 1
@@ -453,7 +511,7 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
         const int r = ch >> 5, c8 = (ch & 31) * 8;
         const int64_t gi = m0 + (r >> 5) * 128 + p * 32 + (r & 31);
         const int64_t gj = n0 + c8;
-        float *src = stg + r * SLD + c8;
+        float *src = stg + srow(r) * SLD + c8;
         const float4 a4 = *reinterpret_cast<const float4 *>(src);
         const float4 b4 = *reinterpret_cast<const float4 *>(src + 4);
         float v[8] = {a4.x, a4.y, a4.z, a4.w, b4.x, b4.y, b4.z, b4.w};
@@ -513,7 +571,7 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
       const int r = ch >> 6, c4 = (ch & 63) * 4;
       const int64_t gi = m0 + (r >> 5) * 128 + p * 32 + (r & 31);
       const int64_t gj = n0 + c4;
-      float *src = stg + r * SLD + c4;
+      float *src = stg + srow(r) * SLD + c4;
       float4 v4 = *reinterpret_cast<const float4 *>(src);
       float v[4] = {v4.x, v4.y, v4.z, v4.w};
       if (gi < M) {
@@ -548,7 +606,35 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
       }
     }
     }
-    if (col_phase) {
+    if (col_phase && fast) {
+      // transposed / mirror stores of an interior tile: lane l of a wave
+      // takes 8-row chunk l % 4 of column c0 + l / 4, so one store
+      // instruction writes 64 contiguous bytes to each of 16 output rows
+      __syncthreads();
+#pragma unroll 2
+      for (int q = 0; q < 8; ++q) {
+        const int ch = tid + NTHR * q;      // 2048 chunks: 2 row groups x 256 columns x 4
+        const int k = ch & 3, c = (ch >> 2) & 255, sg = ch >> 10;
+        const float *col = stg + (sg * 32 + k * 8) * SLD + c;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = col[((e + 2 * k) & 7) * SLD];
+        const int64_t gi = m0 + sg * 128 + p * 32 + k * 8;
+        const int64_t gj = n0 + c;
+        if (osplit) {
+          float hi[8], lo[8];
+          split4(v, hi, lo);
+          split4(v + 4, hi + 4, lo + 4);
+          if (t0 || mirror) {
+            *reinterpret_cast<uint4 *>(S0 + (gj * ld0 + gi) * 2) = pack8(hi);
+            *reinterpret_cast<uint4 *>(S1 + (gj * ld1 + gi) * 2) = pack8(lo);
+          }
+        } else {
+          if (t0 || mirror) *reinterpret_cast<uint4 *>(S0 + (gj * ld0 + gi) * 2) = pack8(v);
+          if (S1 && (t1 || mirror)) *reinterpret_cast<uint4 *>(S1 + (gj * ld1 + gi) * 2) = pack8(v);
+        }
+      }
+    } else if (col_phase) {
       __syncthreads();
 #pragma unroll 1
       for (int q = 0; q < 8; ++q) {
@@ -561,7 +647,7 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
         if (nv <= 0) continue;
         float v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = stg[(r8 + e) * SLD + c];
+        for (int e = 0; e < 8; ++e) v[e] = stg[srow(r8 + e) * SLD + c];
         if (osplit) {
           float hi[8], lo[8];
           split4(v, hi, lo);
