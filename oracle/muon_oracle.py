@@ -305,7 +305,8 @@ class StepResult:
 
 
 def muon_step(grads, state: MuonState, shapes, heads, offsets, num_partitions,
-              partition_numel, opt: MuonOptions, partitions=None) -> StepResult:
+              partition_numel, opt: MuonOptions, partitions=None, grad_scale: float = 1.0,
+              skip: bool = False) -> StepResult:
     """One optimizer step of Muon over a group, on the accumulated gradient
     (PR 8600 "The change": once per step, after accumulation).
 
@@ -313,13 +314,25 @@ def muon_step(grads, state: MuonState, shapes, heads, offsets, num_partitions,
     `state` is updated in place; the Newton-Schulz counter advances by one per
     matrix (PR 8600 table: calls = matrices x steps).  The fp32 partitions are
     written at each matrix's owned intersections with the fp32 value
-    fp32(update); padding is left as given."""
+    fp32(update); padding is left as given.
+
+    grad_scale multiplies every gradient element before the momentum blend:
+    gradients produced under a loss scale S come in with grad_scale = 1/S, so
+    the momentum holds unscaled gradients and the step does not depend on S
+    (the PR 8464 commits validate clipping equivalence across loss scales).
+    skip = True is a step the overflow check discarded: it touches neither
+    momentum nor partitions and counts nothing (PR 8600 "The change": the
+    update runs after the overflow check, so a discarded step leaves the
+    momentum alone)."""
     res = StepResult()
     if partitions is None:
         partitions = [np.zeros(partition_numel, dtype=np.float32)
                       for _ in range(num_partitions)]
+    res.partitions = partitions
+    if skip:
+        return res
     for i, (rows, cols) in enumerate(shapes):
-        g = np.asarray(grads[i], dtype=np.float64).reshape(rows, cols)
+        g = np.asarray(grads[i], dtype=np.float64).reshape(rows, cols) * float(grad_scale)
         m_new, u = momentum_update(state.momenta[i], g, opt.beta, opt.nesterov)
         state.momenta[i] = m_new
         y = muon_matrix_update(u, opt.method, heads[i], opt.steps, opt.coeffs, opt.eps)
@@ -329,8 +342,62 @@ def muon_step(grads, state: MuonState, shapes, heads, offsets, num_partitions,
         res.updates.append(upd)
         scatter_f32(upd.astype(np.float32), offsets[i], partitions)
     state.steps += 1
-    res.partitions = partitions
     return res
+
+
+# ------------------------------------- after the path: norm, clip, apply
+
+
+CLIP_EPS = 1e-6
+
+
+def update_norm(partitions, shapes, offsets) -> float:
+    """L2 norm of the Muon update as the partitions hold it (PR 8600 "The
+    change": the gradient norm is taken over the Muon update): the square
+    root of the sum of squares of every owned element of every matrix, each
+    element counted once, padding excluded."""
+    P = partitions[0].shape[0]
+    total = 0.0
+    for (rows, cols), off in zip(shapes, offsets):
+        for r, o, _j, n in partition_runs(off, rows * cols, P):
+            v = partitions[r][o:o + n].astype(np.float64)
+            total += float(np.dot(v, v))
+    return math.sqrt(total)
+
+
+def clip_coefficient(norm: float, max_norm: float) -> float:
+    """Global-norm clipping factor applied to every update element.  Reading
+    (the pages keep the clipping semantics unchanged without spelling them
+    out): the common convention min(1, max_norm / (norm + 1e-6)), and no
+    clipping when max_norm <= 0."""
+    if max_norm <= 0.0:
+        return 1.0
+    return min(1.0, float(max_norm) / (float(norm) + CLIP_EPS))
+
+
+def apply_update(params, partitions, shapes, offsets, lr: float, weight_decay: float,
+                 max_norm: float, skip: bool = False):
+    """Parameter update from the Muon update in the partitions, on the fp32
+    master partitions `params` (same flat layout).  Reading (the pages stop
+    at the update): decoupled weight decay and a step of size lr along the
+    clipped update,
+        p <- p * (1 - lr * weight_decay) - lr * clip * u,
+    on owned elements only; padding untouched.  Computed in fp64, stored as
+    fp32.  skip = True (a discarded step) leaves params as given.
+    Returns (new params as float32 arrays, norm, clip)."""
+    out = [np.array(p, dtype=np.float32, copy=True) for p in params]
+    if skip:
+        return out, 0.0, 1.0
+    norm = update_norm(partitions, shapes, offsets)
+    clip = clip_coefficient(norm, max_norm)
+    P = partitions[0].shape[0]
+    decay = 1.0 - float(lr) * float(weight_decay)
+    for (rows, cols), off in zip(shapes, offsets):
+        for r, o, _j, n in partition_runs(off, rows * cols, P):
+            p = out[r][o:o + n].astype(np.float64)
+            u = partitions[r][o:o + n].astype(np.float64)
+            out[r][o:o + n] = (p * decay - float(lr) * clip * u).astype(np.float32)
+    return out, norm, clip
 
 
 def gather_from_partitions(partitions, flat_offset: int, rows: int, cols: int) -> np.ndarray:

@@ -112,3 +112,44 @@ def _runs_off_by_one(flat_offset, numel, P):
 def test_layout_pin_catches_index_mistake():
     assert runs_to_index_map(_runs_off_by_one(5, 40, 16), 40) != brute_force_index_map(5, 40, 16)
     assert runs_to_index_map(O.partition_runs(5, 40, 16), 40) == brute_force_index_map(5, 40, 16)
+
+
+# ------------------------------------------- clipping and the param update
+
+
+def _clip_no_clamp(norm, max_norm):
+    return 1.0 if max_norm <= 0 else max_norm / (norm + O.CLIP_EPS)
+
+
+def _clip_inverted(norm, max_norm):
+    return 1.0 if max_norm <= 0 else min(1.0, (norm + O.CLIP_EPS) / max_norm)
+
+
+@pytest.mark.parametrize("bad", [_clip_no_clamp, _clip_inverted])
+def test_clip_pins_catch_mistakes(bad, monkeypatch):
+    monkeypatch.setattr(O, "clip_coefficient", bad)
+    import test_oracle_pins as T
+    with pytest.raises(AssertionError):
+        T.test_clip_coefficient_cases()
+        T.test_apply_update_clipped_step_has_max_norm()
+
+
+_APPLY = O.apply_update
+
+
+def _apply_wrong_sign(params, partitions, shapes, offsets, lr, weight_decay, max_norm, skip=False):
+    return _APPLY(params, partitions, shapes, offsets, -lr, -weight_decay, max_norm, skip)
+
+
+def _apply_coupled_decay(params, partitions, shapes, offsets, lr, weight_decay, max_norm, skip=False):
+    # decay applied to the update instead of the parameter
+    out, norm, clip = _APPLY(params, partitions, shapes, offsets, lr, 0.0, max_norm, skip)
+    return [o * np.float32(1.0 - lr * weight_decay) for o in out], norm, clip
+
+
+@pytest.mark.parametrize("bad", [_apply_wrong_sign, _apply_coupled_decay])
+def test_apply_pins_catch_mistakes(bad, monkeypatch):
+    monkeypatch.setattr(O, "apply_update", bad)
+    import test_oracle_pins as T
+    with pytest.raises(AssertionError):
+        T.test_apply_update_closed_forms()

@@ -326,3 +326,132 @@ def test_step_writes_scaled_update():
         got = O.gather_from_partitions(outs[0].partitions, offsets[i], r, c)
         want = outs[0].ns_out[i] * O.shape_scale(r, c)
         assert O.rel_frobenius(got, want) < 1e-7
+
+
+# ------------------------------------------- loss scale and discarded steps
+
+
+def test_grad_scale_momentum_closed_form():
+    # one step from zero momentum: m = (1 - beta) * s * g exactly as fp32 of
+    # the fp64 product (s a power of two keeps s * g exact)
+    g = W.gaussian((9, 17), 21, 1.0).astype(np.float64)
+    for s in (1.0, 2.0 ** -12, 8.0):
+        state = O.init_state([(9, 17)])
+        O.muon_step([g], state, [(9, 17)], [0], [0], 1, 160, O.MuonOptions(), grad_scale=s)
+        np.testing.assert_array_equal(state.momenta[0], ((1.0 - 0.95) * s * g).astype(np.float32))
+
+
+def test_grad_scale_cancels_loss_scale():
+    # gradients produced under loss scale S, handed in with grad_scale 1/S,
+    # give the unscaled run's momentum and updates (S a power of two: exact)
+    shapes = [(17, 13), (9, 17)]
+    offsets, P = O.pack_layout(shapes, 2)
+    ref_state, sc_state = O.init_state(shapes), O.init_state(shapes)
+    for step in range(2):
+        grads = [W.gaussian(sh, W.grad_seed(0, i, 0, step), 1.0).astype(np.float64) for i, sh in enumerate(shapes)]
+        a = O.muon_step(grads, ref_state, shapes, [0, 0], offsets, 2, P, O.MuonOptions())
+        S = 2.0 ** (10 + step)
+        b = O.muon_step([g * S for g in grads], sc_state, shapes, [0, 0], offsets, 2, P, O.MuonOptions(),
+                        grad_scale=1.0 / S)
+        for i in range(2):
+            np.testing.assert_array_equal(sc_state.momenta[i], ref_state.momenta[i])
+            np.testing.assert_array_equal(b.partitions[i], a.partitions[i])
+
+
+def test_skipped_step_touches_nothing():
+    shapes = [(17, 13), (9, 17)]
+    offsets, P = O.pack_layout(shapes, 2)
+    grads = [W.gaussian(sh, 70 + i, 1.0).astype(np.float64) for i, sh in enumerate(shapes)]
+    state = O.init_state(shapes)
+    O.muon_step(grads, state, shapes, [0, 0], offsets, 2, P, O.MuonOptions())
+    mom = [m.copy() for m in state.momenta]
+    parts = [np.full(P, 7.0, dtype=np.float32) for _ in range(2)]
+    r = O.muon_step([g * np.inf for g in grads], state, shapes, [0, 0], offsets, 2, P, O.MuonOptions(),
+                    partitions=parts, skip=True)
+    assert state.steps == 1 and state.ns_invocations == 2
+    for i in range(2):
+        np.testing.assert_array_equal(state.momenta[i], mom[i])
+        np.testing.assert_array_equal(r.partitions[i], np.full(P, 7.0, dtype=np.float32))
+    # a run with the discarded step in between equals the run without it
+    state2 = O.init_state(shapes)
+    O.muon_step(grads, state2, shapes, [0, 0], offsets, 2, P, O.MuonOptions())
+    g2 = [W.gaussian(sh, 90 + i, 1.0).astype(np.float64) for i, sh in enumerate(shapes)]
+    ra = O.muon_step(g2, state, shapes, [0, 0], offsets, 2, P, O.MuonOptions())
+    rb = O.muon_step(g2, state2, shapes, [0, 0], offsets, 2, P, O.MuonOptions())
+    for i in range(2):
+        np.testing.assert_array_equal(ra.partitions[i], rb.partitions[i])
+
+
+# ----------------------------------------- update norm, clipping, param update
+
+
+def _tiny_layout_with_values():
+    # two matrices 1x2 and 2x2 in two partitions of 4: flat [0..6), padding at
+    # flat 6 and 7 (partition 1, offsets 2 and 3)
+    shapes, offsets, P = [(1, 2), (2, 2)], [0, 2], 4
+    parts = [np.array([3.0, 4.0, 1.0, 2.0], dtype=np.float32),
+             np.array([2.0, 4.0, np.nan, np.nan], dtype=np.float32)]
+    return shapes, offsets, P, parts
+
+
+def test_update_norm_hand_values():
+    shapes, offsets, P, parts = _tiny_layout_with_values()
+    # 9 + 16 + 1 + 4 + 4 + 16 = 50; padding (NaN) excluded
+    assert O.update_norm(parts, shapes, offsets) == pytest.approx(math.sqrt(50.0), abs=1e-15)
+
+
+def test_update_norm_equals_per_matrix_sum():
+    shapes = [(17, 13), (9, 17), (5, 40)]
+    state, outs = _run_group(shapes, 1, 1)
+    offsets, P = O.pack_layout(shapes, 2)
+    parts = outs[0].partitions
+    per = sum(float(np.sum(O.gather_from_partitions(parts, offsets[i], r, c).astype(np.float64) ** 2))
+              for i, (r, c) in enumerate(shapes))
+    assert O.update_norm(parts, shapes, offsets) == pytest.approx(math.sqrt(per), rel=1e-14)
+
+
+def test_clip_coefficient_cases():
+    assert O.clip_coefficient(10.0, 0.0) == 1.0
+    assert O.clip_coefficient(10.0, -1.0) == 1.0
+    assert O.clip_coefficient(0.5, 1.0) == 1.0
+    assert O.clip_coefficient(10.0, 1.0) == pytest.approx(1.0 / (10.0 + 1e-6), rel=1e-15)
+    assert O.clip_coefficient(0.0, 1.0) == 1.0
+
+
+def test_apply_update_closed_forms():
+    shapes, offsets, P, parts = _tiny_layout_with_values()
+    params = [np.array([1.0, -1.0, 0.5, 2.0], dtype=np.float32),
+              np.array([0.25, 8.0, 5.0, -5.0], dtype=np.float32)]
+    # lr = 0: nothing moves
+    out, norm, clip = O.apply_update(params, parts, shapes, offsets, 0.0, 0.1, 0.0)
+    for a, b in zip(out, params):
+        np.testing.assert_array_equal(a, b)
+    # no decay, no clipping: p - lr * u, exact for these values (lr 1/4)
+    out, norm, clip = O.apply_update(params, parts, shapes, offsets, 0.25, 0.0, 0.0)
+    assert clip == 1.0 and norm == pytest.approx(math.sqrt(50.0))
+    np.testing.assert_array_equal(out[0], np.array([0.25, -2.0, 0.25, 1.5], dtype=np.float32))
+    np.testing.assert_array_equal(out[1][:2], np.array([-0.25, 7.0], dtype=np.float32))
+    # padding untouched (the update there is NaN, the params keep their values)
+    np.testing.assert_array_equal(out[1][2:], params[1][2:])
+    # decay only: zero update
+    zero = [np.zeros(4, dtype=np.float32), np.zeros(4, dtype=np.float32)]
+    out, _, _ = O.apply_update(params, zero, shapes, offsets, 0.5, 0.5, 0.0)
+    np.testing.assert_array_equal(out[0], (params[0] * 0.75).astype(np.float32))
+    # skipped step: unchanged
+    out, _, _ = O.apply_update(params, parts, shapes, offsets, 0.25, 0.1, 1.0, skip=True)
+    for a, b in zip(out, params):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_apply_update_clipped_step_has_max_norm():
+    shapes = [(17, 13), (9, 17)]
+    state, outs = _run_group(shapes, 1, 1)
+    offsets, P = O.pack_layout(shapes, 2)
+    parts = outs[0].partitions
+    params = [np.zeros(P, dtype=np.float32) for _ in range(2)]
+    lr, max_norm = 0.5, 0.125
+    out, norm, clip = O.apply_update(params, parts, shapes, offsets, lr, 0.0, max_norm)
+    assert norm > max_norm and clip < 1.0
+    step = [-(o.astype(np.float64)) for o in out]
+    total = math.sqrt(sum(float(np.dot(s, s)) for s in step))
+    assert total == pytest.approx(lr * max_norm * norm / (norm + 1e-6), rel=1e-6)
