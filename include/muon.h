@@ -73,7 +73,8 @@ typedef enum { MUON_NS_STANDARD = 0, MUON_NS_GRAM = 1 } muon_ns_method;
 
 /* Arithmetic of Newton-Schulz.  FP32: fp32 operands and accumulation
  * throughout.  BF16: bf16 MFMA operands with fp32 accumulation; the Gram
- * form's small-side chain (R, P, Q) stays fp32. */
+ * form's small-side chain (R, P, Q) is fp32 for blocks with m < 256 and a
+ * split-bf16 pair (hi + lo, three bf16 products per product) for m >= 256. */
 typedef enum { MUON_PREC_FP32 = 0, MUON_PREC_BF16 = 1 } muon_ns_precision;
 
 /* Storage type of a gradient or update buffer. */
@@ -186,6 +187,56 @@ muon_status muon_accumulate(muon_plan *p, float *const *acc, const void *const *
  * HIP (a launch failed). */
 muon_status muon_step(muon_plan *p, const void *const *grads, float *const *momenta,
                       float *const *partitions, void *ws, size_t ws_bytes, void *stream);
+
+/* muon_step with the two inputs a mixed-precision training loop adds
+ * ([8600] "The change": Muon runs after the overflow check, so a step the
+ * loss scaler discards leaves the momentum untouched; [8464] commits:
+ * results are checked to agree across loss scales):
+ *   skip_flag   DEVICE pointer to an int32, or NULL.  The kernels read it
+ *               when they run: non-zero = a discarded step, and nothing
+ *               outside the workspace is written (momenta and partitions
+ *               keep their contents).  The host never waits for it.  The
+ *               plan's counters still count the call.
+ *   grad_scale  multiplies every gradient element before the momentum blend,
+ *               in fp32 (1/S for gradients produced under loss scale S);
+ *               1.0f gives muon_step bit for bit.  Must be finite.
+ * It also leaves, in the workspace, the per-chunk sums of squares of the
+ * values written to the partitions, for muon_apply_update.
+ * Errors: as muon_step; INVALID_ARG for a non-finite grad_scale, ALIAS if
+ * skip_flag overlaps another buffer. */
+muon_status muon_step_ex(muon_plan *p, const void *const *grads, float *const *momenta,
+                         float *const *partitions, const int32_t *skip_flag, float grad_scale,
+                         void *ws, size_t ws_bytes, void *stream);
+
+/* Overflow check on the step's gradients: *flag (DEVICE int32) = 1 if any
+ * element of any grads[i] (rows x cols, `dtype`) is Inf or NaN, else 0.
+ * The result can be handed to muon_step_ex / muon_apply_update as their
+ * skip flag without a host round trip.  ws/ws_bytes: the plan's workspace
+ * (it holds the matrix table).  Errors: INVALID_ARG, ALIAS, WORKSPACE, HIP. */
+muon_status muon_check_finite(muon_plan *p, const void *const *grads, int32_t dtype,
+                              int32_t *flag, void *ws, size_t ws_bytes, void *stream);
+
+/* The step after the path ([8600] "The change": the gradient norm is taken
+ * over the Muon update, clipping semantics unchanged):
+ *   norm = sqrt(sum of squares of every owned update element), taken from
+ *          the sums the last muon_step / muon_step_ex on this plan and this
+ *          workspace left there (fp64, fixed order: deterministic);
+ *   clip = max_norm > 0 ? min(1, max_norm / (norm + 1e-6)) : 1;
+ *   params[r][j] = params[r][j] * (1 - lr * weight_decay)
+ *                  - (lr * clip) * partitions[r][j]      (fp32, one fma)
+ * on the owned intersections only; padding untouched.
+ *   params[r]      fp32 master partitions, the partitions' layout, updated
+ *   partitions[r]  the update as muon_step wrote it, read only
+ *   skip_flag      DEVICE int32 or NULL: non-zero = nothing is written
+ *   norm_clip_out  DEVICE float[2] or NULL: receives {norm, clip}
+ * Call it after the step, with the same workspace and skip flag, before
+ * the workspace is used by another step.  Errors: INVALID_ARG (NULL
+ * entries, non-finite lr / weight_decay / max_norm, no step on this
+ * workspace), ALIAS, WORKSPACE, HIP. */
+muon_status muon_apply_update(muon_plan *p, float *const *params, const float *const *partitions,
+                              float lr, float weight_decay, float max_norm,
+                              const int32_t *skip_flag, float *norm_clip_out, void *ws,
+                              size_t ws_bytes, void *stream);
 
 /* The writeback alone (the same kernel muon_step ends with): for every
  * matrix i, partitions[r][...] = fp32(updates[i][j]) * fp32(sqrt(max(1,

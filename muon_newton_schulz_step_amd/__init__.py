@@ -10,9 +10,10 @@ from __future__ import annotations
 
 from . import _lib
 from ._lib import (DTYPE, EXPORTS, NS_METHOD, PRECISION, MuonError, load, muon_accumulate,  # noqa: F401
-                   muon_default_options, muon_last_error, muon_layout, muon_plan_create, muon_plan_destroy,
-                   muon_plan_phase_ms, muon_plan_problems, muon_plan_runs, muon_plan_set_timing, muon_plan_stats,
-                   muon_plan_workspace_bytes, muon_scatter, muon_status_string, muon_step)
+                   muon_apply_update, muon_check_finite, muon_default_options, muon_last_error, muon_layout,
+                   muon_plan_create, muon_plan_destroy, muon_plan_phase_ms, muon_plan_problems, muon_plan_runs,
+                   muon_plan_set_timing, muon_plan_stats, muon_plan_workspace_bytes, muon_scatter,
+                   muon_status_string, muon_step, muon_step_ex)
 
 __all__ = ["MuonGroup", "pack_layout", "MuonError", "load"] + list(EXPORTS)
 
@@ -68,8 +69,20 @@ class MuonGroup:
         self.plan = muon_plan_create(mats, o, lay)
         self.workspace_bytes = muon_plan_workspace_bytes(self.plan)
 
-    def step(self, grads, momenta, partitions, ws, stream=None):
-        muon_step(self.plan, grads, momenta, partitions, ws, self.workspace_bytes, stream)
+    def step(self, grads, momenta, partitions, ws, stream=None, skip_flag=None, grad_scale: float = 1.0):
+        if skip_flag is None and grad_scale == 1.0:
+            muon_step(self.plan, grads, momenta, partitions, ws, self.workspace_bytes, stream)
+        else:
+            muon_step_ex(self.plan, grads, momenta, partitions, skip_flag, grad_scale, ws, self.workspace_bytes,
+                         stream)
+
+    def check_finite(self, grads, dtype: str, flag, ws, stream=None):
+        muon_check_finite(self.plan, grads, dtype, flag, ws, self.workspace_bytes, stream)
+
+    def apply_update(self, params, partitions, lr: float, weight_decay: float, max_norm: float, ws,
+                     skip_flag=None, norm_clip_out=None, stream=None):
+        muon_apply_update(self.plan, params, partitions, lr, weight_decay, max_norm, skip_flag, norm_clip_out, ws,
+                          self.workspace_bytes, stream)
 
     def accumulate(self, acc, grad_mb, mb_dtype: str, first: bool, ws, stream=None):
         muon_accumulate(self.plan, acc, grad_mb, mb_dtype, first, ws, self.workspace_bytes, stream)

@@ -26,9 +26,9 @@ DTYPE = {"fp32": 0, "bf16": 1}
 
 # every symbol include/muon.h declares
 EXPORTS = ("muon_default_options", "muon_plan_create", "muon_plan_workspace_bytes", "muon_accumulate",
-           "muon_step", "muon_scatter", "muon_plan_stats", "muon_plan_runs", "muon_plan_problems",
-           "muon_plan_set_timing", "muon_plan_phase_ms", "muon_plan_destroy", "muon_status_string",
-           "muon_last_error")
+           "muon_step", "muon_step_ex", "muon_check_finite", "muon_apply_update", "muon_scatter",
+           "muon_plan_stats", "muon_plan_runs", "muon_plan_problems", "muon_plan_set_timing",
+           "muon_plan_phase_ms", "muon_plan_destroy", "muon_status_string", "muon_last_error")
 
 
 class muon_matrix(C.Structure):
@@ -82,6 +82,10 @@ def load(path: str | None = None) -> C.CDLL:
         "muon_plan_workspace_bytes": (i32, [vp, C.POINTER(sz)]),
         "muon_accumulate": (i32, [vp, C.POINTER(vp), C.POINTER(vp), i32, i32, vp, sz, vp]),
         "muon_step": (i32, [vp, C.POINTER(vp), C.POINTER(vp), C.POINTER(vp), vp, sz, vp]),
+        "muon_step_ex": (i32, [vp, C.POINTER(vp), C.POINTER(vp), C.POINTER(vp), vp, C.c_float, vp, sz, vp]),
+        "muon_check_finite": (i32, [vp, C.POINTER(vp), i32, vp, vp, sz, vp]),
+        "muon_apply_update": (i32, [vp, C.POINTER(vp), C.POINTER(vp), C.c_float, C.c_float, C.c_float, vp, vp,
+                                    vp, sz, vp]),
         "muon_scatter": (i32, [vp, C.POINTER(vp), i32, C.POINTER(vp), vp, sz, vp]),
         "muon_plan_stats": (i32, [vp, C.POINTER(muon_stats)]),
         "muon_plan_runs": (i32, [vp, i32, C.POINTER(muon_run), i32, C.POINTER(i32)]),
@@ -178,6 +182,25 @@ def muon_accumulate(plan, acc, grad_mb, mb_dtype: str, first: bool, ws, ws_bytes
 def muon_step(plan, grads, momenta, partitions, ws, ws_bytes: int, stream=None) -> None:
     _check(load().muon_step(plan, _ptr_table(grads), _ptr_table(momenta), _ptr_table(partitions), _ptr(ws),
                             int(ws_bytes), _stream(stream)), "muon_step")
+
+
+def muon_step_ex(plan, grads, momenta, partitions, skip_flag, grad_scale: float, ws, ws_bytes: int,
+                 stream=None) -> None:
+    _check(load().muon_step_ex(plan, _ptr_table(grads), _ptr_table(momenta), _ptr_table(partitions),
+                               _ptr(skip_flag), float(grad_scale), _ptr(ws), int(ws_bytes), _stream(stream)),
+           "muon_step_ex")
+
+
+def muon_check_finite(plan, grads, dtype: str, flag, ws, ws_bytes: int, stream=None) -> None:
+    _check(load().muon_check_finite(plan, _ptr_table(grads), _dt(dtype), _ptr(flag), _ptr(ws), int(ws_bytes),
+                                    _stream(stream)), "muon_check_finite")
+
+
+def muon_apply_update(plan, params, partitions, lr: float, weight_decay: float, max_norm: float, skip_flag,
+                      norm_clip_out, ws, ws_bytes: int, stream=None) -> None:
+    _check(load().muon_apply_update(plan, _ptr_table(params), _ptr_table(partitions), float(lr),
+                                    float(weight_decay), float(max_norm), _ptr(skip_flag), _ptr(norm_clip_out),
+                                    _ptr(ws), int(ws_bytes), _stream(stream)), "muon_apply_update")
 
 
 def muon_scatter(plan, updates, dtype: str, partitions, ws, ws_bytes: int, stream=None) -> None:

@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <cstddef>
+#include <cmath>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -116,7 +117,13 @@ extern "C" {
 
 muon_status muon_step(muon_plan *p, const void *const *grads, float *const *momenta, float *const *partitions, void *ws,
                       size_t ws_bytes, void *stream) {
+  return muon_step_ex(p, grads, momenta, partitions, nullptr, 1.0f, ws, ws_bytes, stream);
+}
+
+muon_status muon_step_ex(muon_plan *p, const void *const *grads, float *const *momenta, float *const *partitions,
+                         const int32_t *skip_flag, float grad_scale, void *ws, size_t ws_bytes, void *stream) {
   if (!p || !grads || !momenta || !partitions) { set_error("muon_step: NULL argument"); return MUON_ERR_INVALID_ARG; }
+  if (!std::isfinite(grad_scale)) { set_error("muon_step: grad_scale is not finite"); return MUON_ERR_INVALID_ARG; }
   const int32_t nmat = (int32_t)p->mats.size();
   const int32_t R = p->layout.num_partitions;
   const size_t gsz = dtype_size(p->opt.grad_dtype);
@@ -136,6 +143,7 @@ muon_status muon_step(muon_plan *p, const void *const *grads, float *const *mome
   muon_status st = check_ws(p, ws, ws_bytes, (size_t)p->ws_bytes);
   if (st != MUON_OK) return st;
   rs.push_back({(uintptr_t)ws, (uintptr_t)ws + ws_bytes, "workspace", 0});
+  if (skip_flag) rs.push_back({(uintptr_t)skip_flag, (uintptr_t)skip_flag + 4, "skip_flag", 0});
   if ((st = check_alias(rs)) != MUON_OK) return st;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -177,6 +185,7 @@ muon_status muon_step(muon_plan *p, const void *const *grads, float *const *mome
   const bool gbf16 = p->opt.grad_dtype == MUON_DT_BF16;
   float *partials = reinterpret_cast<float *>(wsb + p->partials_off);
   float *scales = reinterpret_cast<float *>(wsb + p->scales_off);
+  float *nparts = reinterpret_cast<float *>(wsb + p->nparts_off);
   hipError_t e;
   for (const WavePlan &W : p->waves) {
     const int np = (int)W.probs.size();
@@ -184,12 +193,14 @@ muon_status muon_step(muon_plan *p, const void *const *grads, float *const *mome
     const ProbDev *probs = reinterpret_cast<const ProbDev *>(wsb + W.off_prob);
     const K3Run *runs = reinterpret_cast<const K3Run *>(wsb + W.off_runs);
     if ((e = mark(wi, 0)) != hipSuccess) return hip_fail(e, "hipEventRecord (timing)");
-    if ((e = launch_k1(k1, np, W.k1_tiles, wsb, partials, p->opt.beta, p->opt.nesterov, gbf16, s)) != hipSuccess)
+    if ((e = launch_k1(k1, np, W.k1_tiles, wsb, partials, p->opt.beta, p->opt.nesterov, grad_scale, skip_flag, gbf16,
+                       s)) != hipSuccess)
       return hip_fail(e, "K1 launch");
-    if ((e = launch_kn(k1, np, partials, scales, p->opt.eps, s)) != hipSuccess) return hip_fail(e, "norm launch");
+    if ((e = launch_kn(k1, np, partials, scales, p->opt.eps, skip_flag, s)) != hipSuccess)
+      return hip_fail(e, "norm launch");
     if ((e = mark(wi, 1)) != hipSuccess) return hip_fail(e, "hipEventRecord (timing)");
     if (p->opt.ns_steps == 0) {
-      if ((e = launch_kc(probs, k1, np, wsb, scales, s)) != hipSuccess) return hip_fail(e, "copy launch");
+      if ((e = launch_kc(probs, k1, np, wsb, scales, skip_flag, s)) != hipSuccess) return hip_fail(e, "copy launch");
     } else {
       // large bf16 problems first (the bulk of the work), then small bf16
       // ones, then fp32-operand ones
@@ -201,7 +212,7 @@ muon_status muon_step(muon_plan *p, const void *const *grads, float *const *mome
           const int list = big ? (L.mn ? TL_MN256 : TL_MM256) : (L.mn ? TL_MN128 : TL_MM128);
           const TileDev *tl = reinterpret_cast<const TileDev *>(wsb + W.off_tiles[grp][list]);
           const int nt = (int)W.tiles[grp][list].size();
-          GemmArgs a{probs, tl, wsb, scales, L.r};
+          GemmArgs a{probs, tl, wsb, scales, L.r, skip_flag};
           e = big ? launch_gemm256(a, nt, s) : launch_gemm(L.kind == Launch::GEMM_OP, a, nt, s);
           if (e != hipSuccess) return hip_fail(e, "Newton-Schulz launch");
           ++ns_launches;
@@ -209,7 +220,8 @@ muon_status muon_step(muon_plan *p, const void *const *grads, float *const *mome
       }
     }
     if ((e = mark(wi, 2)) != hipSuccess) return hip_fail(e, "hipEventRecord (timing)");
-    if ((e = launch_k3(runs, (int)W.runs.size(), W.k3_chunks, s)) != hipSuccess) return hip_fail(e, "K3 launch");
+    if ((e = launch_k3(runs, (int)W.runs.size(), W.k3_chunks, skip_flag, nparts, W.k3_base, s)) != hipSuccess)
+      return hip_fail(e, "K3 launch");
     if ((e = mark(wi, 3)) != hipSuccess) return hip_fail(e, "hipEventRecord (timing)");
     ++wi;
   }
@@ -219,6 +231,7 @@ muon_status muon_step(muon_plan *p, const void *const *grads, float *const *mome
   }
   p->stats.steps += 1;
   p->stats.ns_invocations += (uint64_t)nmat;
+  p->norm_ws = ws;
   return MUON_OK;
 }
 
@@ -302,8 +315,100 @@ muon_status muon_scatter(muon_plan *p, const void *const *updates, int32_t dtype
   if ((st = acquire_slot(p, std::max<size_t>(tb, p->host_tables.size()), &h, &slot)) != MUON_OK) return st;
   std::memcpy(h, tab.data(), tb);
   if ((st = upload(p, slot, ws, tb, s)) != MUON_OK) return st;
-  hipError_t e = launch_k3(static_cast<const K3Run *>(ws), (int)tab.size(), ch, s);
+  hipError_t e = launch_k3(static_cast<const K3Run *>(ws), (int)tab.size(), ch, nullptr, nullptr, 0, s);
   if (e != hipSuccess) return hip_fail(e, "scatter launch");
+  return MUON_OK;
+}
+
+muon_status muon_check_finite(muon_plan *p, const void *const *grads, int32_t dtype, int32_t *flag, void *ws,
+                              size_t ws_bytes, void *stream) {
+  if (!p || !grads || !flag) { set_error("muon_check_finite: NULL argument"); return MUON_ERR_INVALID_ARG; }
+  if (dtype != MUON_DT_FP32 && dtype != MUON_DT_BF16) { set_error("muon_check_finite: unknown dtype"); return MUON_ERR_INVALID_ARG; }
+  const int32_t nmat = (int32_t)p->mats.size();
+  const size_t gsz = dtype_size(dtype);
+  std::vector<Range> rs;
+  std::vector<K0Mat> tab(nmat);
+  int64_t ch = 0;
+  for (int32_t i = 0; i < nmat; ++i) {
+    if (!grads[i]) { set_error("muon_check_finite: NULL grads entry " + std::to_string(i)); return MUON_ERR_INVALID_ARG; }
+    const int64_t n = p->mats[i].desc.rows * p->mats[i].desc.cols;
+    rs.push_back({(uintptr_t)grads[i], (uintptr_t)grads[i] + (uintptr_t)n * gsz, "grads", i});
+    tab[i] = K0Mat{nullptr, grads[i], n, ch};
+    ch += (n + K0_CHUNK - 1) / K0_CHUNK;
+  }
+  const size_t tb = tab.size() * sizeof(K0Mat);
+  muon_status st = check_ws(p, ws, ws_bytes, tb);
+  if (st != MUON_OK) return st;
+  rs.push_back({(uintptr_t)ws, (uintptr_t)ws + ws_bytes, "workspace", 0});
+  rs.push_back({(uintptr_t)flag, (uintptr_t)flag + 4, "flag", 0});
+  if ((st = check_alias(rs)) != MUON_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char *h = nullptr;
+  int slot = 0;
+  if ((st = acquire_slot(p, std::max<size_t>(tb, p->host_tables.size()), &h, &slot)) != MUON_OK) return st;
+  std::memcpy(h, tab.data(), tb);
+  if ((st = upload(p, slot, ws, tb, s)) != MUON_OK) return st;
+  hipError_t e = launch_finite(static_cast<const K0Mat *>(ws), nmat, ch, dtype == MUON_DT_BF16, flag, s);
+  if (e != hipSuccess) return hip_fail(e, "finite-check launch");
+  return MUON_OK;
+}
+
+muon_status muon_apply_update(muon_plan *p, float *const *params, const float *const *partitions, float lr,
+                              float weight_decay, float max_norm, const int32_t *skip_flag, float *norm_clip_out,
+                              void *ws, size_t ws_bytes, void *stream) {
+  if (!p || !params || !partitions) { set_error("muon_apply_update: NULL argument"); return MUON_ERR_INVALID_ARG; }
+  if (!std::isfinite(lr) || !std::isfinite(weight_decay) || !std::isfinite(max_norm)) {
+    set_error("muon_apply_update: lr, weight_decay and max_norm must be finite");
+    return MUON_ERR_INVALID_ARG;
+  }
+  muon_status st = check_ws(p, ws, ws_bytes, (size_t)p->ws_bytes);
+  if (st != MUON_OK) return st;
+  if (p->norm_ws != ws) {
+    set_error("muon_apply_update: no muon_step has run on this plan with this workspace");
+    return MUON_ERR_INVALID_ARG;
+  }
+  const int32_t R = p->layout.num_partitions;
+  const uintptr_t pb = (uintptr_t)p->layout.partition_numel * 4;
+  std::vector<Range> rs;
+  for (int32_t r = 0; r < R; ++r) {
+    if (!params[r] || !partitions[r]) {
+      set_error("muon_apply_update: NULL params/partitions entry " + std::to_string(r));
+      return MUON_ERR_INVALID_ARG;
+    }
+    rs.push_back({(uintptr_t)params[r], (uintptr_t)params[r] + pb, "params", r});
+    rs.push_back({(uintptr_t)partitions[r], (uintptr_t)partitions[r] + pb, "partitions", r});
+  }
+  rs.push_back({(uintptr_t)ws, (uintptr_t)ws + ws_bytes, "workspace", 0});
+  if (skip_flag) rs.push_back({(uintptr_t)skip_flag, (uintptr_t)skip_flag + 4, "skip_flag", 0});
+  if (norm_clip_out) rs.push_back({(uintptr_t)norm_clip_out, (uintptr_t)norm_clip_out + 8, "norm_clip_out", 0});
+  if ((st = check_alias(rs)) != MUON_OK) return st;
+  std::vector<KARun> tab;
+  int64_t ch = 0;
+  for (const auto &M : p->mats) {
+    for (const muon_run &r : M.runs) {
+      KARun k;
+      k.param = params[r.partition] + r.offset;
+      k.upd = partitions[r.partition] + r.offset;
+      k.length = r.length;
+      k.chunk0 = ch;
+      ch += (r.length + KA_CHUNK - 1) / KA_CHUNK;
+      tab.push_back(k);
+    }
+  }
+  const size_t tb = tab.size() * sizeof(KARun);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char *h = nullptr;
+  int slot = 0;
+  if ((st = acquire_slot(p, std::max<size_t>(tb, p->host_tables.size()), &h, &slot)) != MUON_OK) return st;
+  std::memcpy(h, tab.data(), tb);
+  if ((st = upload(p, slot, ws, tb, s)) != MUON_OK) return st;
+  char *wsb = static_cast<char *>(ws);
+  const float *nparts = reinterpret_cast<const float *>(wsb + p->nparts_off);
+  float *nc = reinterpret_cast<float *>(wsb + p->nc_off);
+  hipError_t e = launch_norm_clip(nparts, p->nparts_n, max_norm, nc, norm_clip_out, skip_flag, s);
+  if (e != hipSuccess) return hip_fail(e, "norm launch");
+  e = launch_apply(static_cast<const KARun *>(ws), (int)tab.size(), ch, nc, lr, weight_decay, skip_flag, s);
+  if (e != hipSuccess) return hip_fail(e, "apply launch");
   return MUON_OK;
 }
 

@@ -146,7 +146,9 @@ __device__ __forceinline__ void store4(void *p, int64_t i, const float *v, bool 
 // 4-row quad of one column per access, read from the LDS tile.
 template <bool GBF16>
 __global__ __launch_bounds__(256) void k1_momentum(const K1Prob *probs, int nprob, char *ws, float *partials,
-                                                   float beta, float omb, int nesterov) {
+                                                   float beta, float omb, int nesterov, float gs,
+                                                   const int32_t *skip) {
+  if (skip && *skip) return;
   __shared__ float tile[K1_TILE][K1_TILE + 1];
   __shared__ float red[4];
   const int t = blockIdx.x;
@@ -164,7 +166,7 @@ __global__ __launch_bounds__(256) void k1_momentum(const K1Prob *probs, int npro
   const int cq = tx * 4;
   const int64_t c = c0 + cq;
   auto one = [&](float g, float m, float &mn, float &u) {
-    const float og = omb * g;
+    const float og = omb * (g * gs);
     mn = fmaf(beta, m, og);
     u = nesterov ? fmaf(beta, mn, og) : mn;
   };
@@ -232,7 +234,8 @@ __global__ __launch_bounds__(256) void k1_momentum(const K1Prob *probs, int npro
 // ----------------------------------------------------------------- KN
 
 __global__ __launch_bounds__(256) void kn_finalize(const K1Prob *probs, const float *partials, float *scales,
-                                                   float eps) {
+                                                   float eps, const int32_t *skip) {
+  if (skip && *skip) return;
   __shared__ double red[256];
   const K1Prob P = probs[blockIdx.x];
   double s = 0.0;
@@ -252,10 +255,12 @@ __global__ __launch_bounds__(256) void kn_finalize(const K1Prob *probs, const fl
 // ----------------------------------------------------------------- K3
 
 // One IEEE multiply per element.  8 elements per lane when the chunk's
-// source and destination are 16-byte aligned.
+// source and destination are 16-byte aligned.  Returns this thread's sum of
+// squares of the values it wrote, in its own element order.
 template <bool SBF16>
-__device__ __forceinline__ void k3_body(const K3Run &R, int64_t start, int64_t end) {
+__device__ __forceinline__ float k3_body(const K3Run &R, int64_t start, int64_t end) {
   const void *src = R.src;
+  float ss = 0.f;
   const bool vec = aligned16(R.dst + start) &&
                    aligned16(SBF16 ? (const void *)(static_cast<const uint16_t *>(src) + R.first + start)
                                    : (const void *)(static_cast<const float *>(src) + R.first + start));
@@ -265,30 +270,134 @@ __device__ __forceinline__ void k3_body(const K3Run &R, int64_t start, int64_t e
       float v[8];
       load8<SBF16>(src, R.first + j, v);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = v[k] * R.scale;
+      for (int k = 0; k < 8; ++k) {
+        v[k] = v[k] * R.scale;
+        ss = fmaf(v[k], v[k], ss);
+      }
       store8_f32(R.dst + j, v);
     }
-    for (j = start + (end - start) / 8 * 8 + threadIdx.x; j < end; j += 256)
-      R.dst[j] = load_as_f32<SBF16>(src, R.first + j) * R.scale;
-    return;
+    for (j = start + (end - start) / 8 * 8 + threadIdx.x; j < end; j += 256) {
+      const float v = load_as_f32<SBF16>(src, R.first + j) * R.scale;
+      R.dst[j] = v;
+      ss = fmaf(v, v, ss);
+    }
+    return ss;
   }
-  for (int64_t j = start + threadIdx.x; j < end; j += 256) R.dst[j] = load_as_f32<SBF16>(src, R.first + j) * R.scale;
+  for (int64_t j = start + threadIdx.x; j < end; j += 256) {
+    const float v = load_as_f32<SBF16>(src, R.first + j) * R.scale;
+    R.dst[j] = v;
+    ss = fmaf(v, v, ss);
+  }
+  return ss;
 }
 
-__global__ __launch_bounds__(256) void k3_scatter(const K3Run *runs, int nrun) {
+// Workgroup sum of one value per thread in a fixed order: wave butterfly,
+// then the four waves in index order.  Result valid in thread 0.
+__device__ __forceinline__ float block_sum_fixed(float v) {
+  __shared__ float red[4];
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+__global__ __launch_bounds__(256) void k3_scatter(const K3Run *runs, int nrun, const int32_t *skip, float *nparts,
+                                                  int64_t pbase) {
+  if (skip && *skip) return;
   const int64_t ch = blockIdx.x;
   const int i = find_owner(nrun, ch, [&](int k) { return runs[k].chunk0; });
   const K3Run R = runs[i];
   const int64_t start = (ch - R.chunk0) * K3_CHUNK;
   const int64_t end = min(start + (int64_t)K3_CHUNK, R.length);
-  if (R.src_bf16) k3_body<true>(R, start, end);
-  else k3_body<false>(R, start, end);
+  const float ss = R.src_bf16 ? k3_body<true>(R, start, end) : k3_body<false>(R, start, end);
+  if (nparts) {
+    const float t = block_sum_fixed(ss);
+    if (threadIdx.x == 0) nparts[pbase + ch] = t;
+  }
+}
+
+// ----------------------------------------------------------------- finite check
+
+__global__ __launch_bounds__(64) void kf_zero(int32_t *flag) {
+  if (threadIdx.x == 0) *flag = 0;
+}
+
+template <bool GBF16>
+__global__ __launch_bounds__(256) void kf_scan(const K0Mat *mats, int nmat, int32_t *flag) {
+  const int64_t ch = blockIdx.x;
+  const int i = find_owner(nmat, ch, [&](int k) { return mats[k].chunk0; });
+  const void *g = mats[i].g;
+  const int64_t start = (ch - mats[i].chunk0) * K0_CHUNK;
+  const int64_t end = min(start + (int64_t)K0_CHUNK, mats[i].numel);
+  int bad = 0;
+  for (int64_t j = start + threadIdx.x; j < end; j += 256) {
+    const float v = load_as_f32<GBF16>(g, j);
+    bad |= !isfinite(v);
+  }
+  // every writer stores the same value 1, so concurrent stores agree
+  if (__syncthreads_or(bad) && threadIdx.x == 0) *flag = 1;
+}
+
+// ----------------------------------------------------------------- norm, clip, apply
+
+__global__ __launch_bounds__(256) void k_norm_clip(const float *nparts, int64_t n, float max_norm, float *nc,
+                                                   float *user_out, const int32_t *skip) {
+  if (skip && *skip) return;
+  __shared__ double red[256];
+  double s = 0.0;
+  for (int64_t i = threadIdx.x; i < n; i += 256) s += (double)nparts[i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double norm = sqrt(red[0]);
+    double clip = 1.0;
+    if (max_norm > 0.f) clip = fmin(1.0, (double)max_norm / (norm + 1e-6));
+    nc[0] = (float)norm;
+    nc[1] = (float)clip;
+    if (user_out) {
+      user_out[0] = (float)norm;
+      user_out[1] = (float)clip;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_apply(const KARun *runs, int nrun, const float *nc, float lr, float wd,
+                                               const int32_t *skip) {
+  if (skip && *skip) return;
+  const int64_t ch = blockIdx.x;
+  const int i = find_owner(nrun, ch, [&](int k) { return runs[k].chunk0; });
+  const KARun R = runs[i];
+  const int64_t start = (ch - R.chunk0) * KA_CHUNK;
+  const int64_t end = min(start + (int64_t)KA_CHUNK, R.length);
+  const float decay = 1.0f - lr * wd;
+  const float step = lr * nc[1];
+  auto one = [&](float p, float u) { return fmaf(-step, u, p * decay); };
+  if (aligned16(R.param + start) && aligned16(R.upd + start)) {
+    int64_t j;
+    for (j = start + 8 * threadIdx.x; j + 8 <= end; j += 8 * 256) {
+      float p[8], u[8];
+      load8<false>(R.param, j, p);
+      load8<false>(R.upd, j, u);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) p[k] = one(p[k], u[k]);
+      store8_f32(R.param + j, p);
+    }
+    for (j = start + (end - start) / 8 * 8 + threadIdx.x; j < end; j += 256) R.param[j] = one(R.param[j], R.upd[j]);
+    return;
+  }
+  for (int64_t j = start + threadIdx.x; j < end; j += 256) R.param[j] = one(R.param[j], R.upd[j]);
 }
 
 // ----------------------------------------------------------------- KC
 
 __global__ __launch_bounds__(256) void kc_copy_scaled(const ProbDev *probs, const K1Prob *k1, char *ws,
-                                                      const float *scales) {
+                                                      const float *scales, const int32_t *skip) {
+  if (skip && *skip) return;
   const int p = blockIdx.x;
   const K1Prob K = k1[p];
   const ProbDev D = probs[p];
@@ -313,30 +422,57 @@ hipError_t launch_k0(const K0Mat *mats, int nmat, int64_t chunks, bool gbf16, in
 }
 
 hipError_t launch_k1(const K1Prob *probs, int nprob, int tiles, char *ws, float *partials, float beta, int nesterov,
-                     bool gbf16, hipStream_t s) {
+                     float grad_scale, const int32_t *skip, bool gbf16, hipStream_t s) {
   if (tiles <= 0) return hipSuccess;
   const float omb = 1.0f - beta;
   dim3 g((unsigned)tiles), b(256);
-  if (gbf16) hipLaunchKernelGGL(k1_momentum<true>, g, b, 0, s, probs, nprob, ws, partials, beta, omb, nesterov);
-  else hipLaunchKernelGGL(k1_momentum<false>, g, b, 0, s, probs, nprob, ws, partials, beta, omb, nesterov);
+  if (gbf16)
+    hipLaunchKernelGGL(k1_momentum<true>, g, b, 0, s, probs, nprob, ws, partials, beta, omb, nesterov, grad_scale, skip);
+  else
+    hipLaunchKernelGGL(k1_momentum<false>, g, b, 0, s, probs, nprob, ws, partials, beta, omb, nesterov, grad_scale, skip);
   return hipGetLastError();
 }
 
-hipError_t launch_kn(const K1Prob *probs, int nprob, const float *partials, float *scales, float eps, hipStream_t s) {
+hipError_t launch_kn(const K1Prob *probs, int nprob, const float *partials, float *scales, float eps,
+                     const int32_t *skip, hipStream_t s) {
   if (nprob <= 0) return hipSuccess;
-  hipLaunchKernelGGL(kn_finalize, dim3(nprob), dim3(256), 0, s, probs, partials, scales, eps);
+  hipLaunchKernelGGL(kn_finalize, dim3(nprob), dim3(256), 0, s, probs, partials, scales, eps, skip);
   return hipGetLastError();
 }
 
-hipError_t launch_k3(const K3Run *runs, int nrun, int64_t chunks, hipStream_t s) {
+hipError_t launch_k3(const K3Run *runs, int nrun, int64_t chunks, const int32_t *skip, float *nparts, int64_t pbase,
+                     hipStream_t s) {
   if (chunks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k3_scatter, dim3((unsigned)chunks), dim3(256), 0, s, runs, nrun);
+  hipLaunchKernelGGL(k3_scatter, dim3((unsigned)chunks), dim3(256), 0, s, runs, nrun, skip, nparts, pbase);
   return hipGetLastError();
 }
 
-hipError_t launch_kc(const ProbDev *probs, const K1Prob *k1, int nprob, char *ws, const float *scales, hipStream_t s) {
+hipError_t launch_kc(const ProbDev *probs, const K1Prob *k1, int nprob, char *ws, const float *scales,
+                     const int32_t *skip, hipStream_t s) {
   if (nprob <= 0) return hipSuccess;
-  hipLaunchKernelGGL(kc_copy_scaled, dim3(nprob), dim3(256), 0, s, probs, k1, ws, scales);
+  hipLaunchKernelGGL(kc_copy_scaled, dim3(nprob), dim3(256), 0, s, probs, k1, ws, scales, skip);
+  return hipGetLastError();
+}
+
+hipError_t launch_finite(const K0Mat *mats, int nmat, int64_t chunks, bool gbf16, int32_t *flag, hipStream_t s) {
+  hipLaunchKernelGGL(kf_zero, dim3(1), dim3(64), 0, s, flag);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || chunks <= 0) return e;
+  if (gbf16) hipLaunchKernelGGL(kf_scan<true>, dim3((unsigned)chunks), dim3(256), 0, s, mats, nmat, flag);
+  else hipLaunchKernelGGL(kf_scan<false>, dim3((unsigned)chunks), dim3(256), 0, s, mats, nmat, flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_clip(const float *nparts, int64_t n, float max_norm, float *nc, float *user_out,
+                            const int32_t *skip, hipStream_t s) {
+  hipLaunchKernelGGL(k_norm_clip, dim3(1), dim3(256), 0, s, nparts, n, max_norm, nc, user_out, skip);
+  return hipGetLastError();
+}
+
+hipError_t launch_apply(const KARun *runs, int nrun, int64_t chunks, const float *nc, float lr, float wd,
+                        const int32_t *skip, hipStream_t s) {
+  if (chunks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_apply, dim3((unsigned)chunks), dim3(256), 0, s, runs, nrun, nc, lr, wd, skip);
   return hipGetLastError();
 }
 

@@ -70,6 +70,7 @@ __device__ __forceinline__ uint4 mask_tail(uint4 v, int valid) {
 
 template <bool BF16>
 __global__ __launch_bounds__(NTHR) void ns_gemm(GemmArgs args) {
+  if (args.skip && *args.skip) return;
   constexpr int ES = BF16 ? 2 : 4;   // operand element bytes
   constexpr int BK = 64 / ES;        // K elements per staged row
   constexpr int EPC = 16 / ES;       // elements per 16-byte chunk

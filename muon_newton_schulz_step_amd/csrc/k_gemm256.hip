@@ -194,6 +194,7 @@ __device__ __forceinline__ uint4 mask_tail_bf16(uint4 v, int valid) {
 template <bool SPLIT>
 __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles) {
   __shared__ __attribute__((aligned(1024))) char lds[2 * 2 * OPB];
+  if (args.skip && *args.skip) return;
 
 #if MUON_XCD_REMAP
   // Workgroup i runs on XCD i % 8.  The tile list is cut into chunks of

@@ -288,7 +288,7 @@ muon_status build_plan(muon_plan *p) {
   p->schedule[1] = build_schedule(o, true);
   p->schedule[2] = standard ? p->schedule[1] : build_split_gram_schedule(o);
 
-  int64_t max_k1 = 0, max_probs = 0, max_data = 0;
+  int64_t max_k1 = 0, max_probs = 0, max_data = 0, nparts = 0;
   for (size_t w = 0; w < p->waves.size(); ++w) {
     WavePlan &W = p->waves[w];
     Carver dat;
@@ -426,6 +426,8 @@ muon_status build_plan(muon_plan *p) {
       }
     }
     W.k3_chunks = ch;
+    W.k3_base = nparts;
+    nparts += ch;
     W.off_prob = tab.take((int64_t)W.probs.size() * sizeof(ProbDev));
     W.off_k1 = tab.take((int64_t)W.k1.size() * sizeof(K1Prob));
     for (int g = 0; g < NGROUPS; ++g)
@@ -436,7 +438,8 @@ muon_status build_plan(muon_plan *p) {
   int64_t scatter_runs = 0;
   for (auto &M : p->mats) scatter_runs += (int64_t)M.runs.size();
   p->k0_table_bytes = std::max<int64_t>(rup(nmat * (int64_t)sizeof(K0Mat), kAlign),
-                                         rup(scatter_runs * (int64_t)sizeof(K3Run), kAlign));
+                                         std::max(rup(scatter_runs * (int64_t)sizeof(K3Run), kAlign),
+                                                  rup(scatter_runs * (int64_t)sizeof(KARun), kAlign)));
   p->tables_bytes = std::max(rup(tab.top, kAlign), p->k0_table_bytes);
   p->max_k1_tiles = max_k1;
   p->max_probs = max_probs;
@@ -444,6 +447,9 @@ muon_status build_plan(muon_plan *p) {
   ws.take(p->tables_bytes);
   p->partials_off = ws.take(std::max<int64_t>(max_k1, 1) * 4);
   p->scales_off = ws.take(std::max<int64_t>(max_probs, 1) * 4);
+  p->nparts_n = nparts;
+  p->nparts_off = ws.take(std::max<int64_t>(nparts, 1) * 4);
+  p->nc_off = ws.take(2 * 4);
   p->data_off = ws.take(max_data);
   p->ws_bytes = rup(ws.top, kAlign);
   // absolute offsets inside the workspace

@@ -56,6 +56,7 @@ struct WavePlan {
   std::vector<int32_t> k1_matrix;    // matrix of each K1 problem
   int32_t k1_tiles = 0;
   int64_t k3_chunks = 0;
+  int64_t k3_base = 0;   // index of this wave's first K3 chunk over all waves
 };
 
 // Step of the launch schedule.
@@ -80,6 +81,9 @@ struct muon_plan {
   int64_t partials_off = 0, scales_off = 0, data_off = 0, ws_bytes = 0;
   int64_t max_k1_tiles = 0, max_probs = 0;
   int64_t k0_table_bytes = 0;  // accumulation table (shares the table region)
+  // update norm: per-K3-chunk sums of squares (all waves), then [norm, clip]
+  int64_t nparts_off = 0, nparts_n = 0, nc_off = 0;
+  const void *norm_ws = nullptr;  // workspace of the last muon_step (its partials are current)
   std::vector<char> host_tables;  // serialized tables (pointers patched per call)
   // lazily created HIP resources (pinned staging, events), see abi.cpp
   void *staging[2] = {nullptr, nullptr};

@@ -89,6 +89,15 @@ struct K3Run {
 };
 constexpr int K3_CHUNK = 4096;  // elements per K3 workgroup
 
+// One owned run of the parameter update (the same runs as the writeback).
+struct KARun {
+  float *param;          // fp32 master partition base + local offset of the run
+  const float *upd;      // update partition base + the same offset
+  int64_t length;
+  int64_t chunk0;        // first chunk of this run (prefix)
+};
+constexpr int KA_CHUNK = 4096;
+
 // One matrix of an accumulation call.
 struct K0Mat {
   float *acc;

@@ -156,3 +156,46 @@ def test_step_validation_fails_before_device():
         M.muon_scatter(g.plan, grads, 7, parts, ws, ws_bytes, 0)
     assert ei.value.name == "MUON_ERR_INVALID_ARG"
     assert g.stats()["steps"] == 0 and g.stats()["ns_invocations"] == 0
+
+
+def test_step_ex_check_and_apply_validation_fails_before_device():
+    g = _group([(8, 8), (4, 12)], grad_dtype="fp32", precision="fp32")
+    ws_bytes = g.workspace_bytes
+    base = 1 << 40
+    ws = base + (1 << 30)
+    grads = [base, base + 4096]
+    moms = [base + 8192, base + 12288]
+    parts = [base + 16384]
+    params = [base + 32768]
+    flag = base + 65536
+    # grad_scale must be finite
+    for bad in (float("inf"), float("nan")):
+        with pytest.raises(M.MuonError) as ei:
+            M.muon_step_ex(g.plan, grads, moms, parts, flag, bad, ws, ws_bytes, 0)
+        assert ei.value.name == "MUON_ERR_INVALID_ARG"
+    # the skip flag may not overlap another buffer of the call
+    with pytest.raises(M.MuonError) as ei:
+        M.muon_step_ex(g.plan, grads, moms, parts, moms[0] + 4, 1.0, ws, ws_bytes, 0)
+    assert ei.value.name == "MUON_ERR_ALIAS"
+    # finite check: unknown dtype, NULL flag, flag inside a gradient
+    with pytest.raises(M.MuonError) as ei:
+        M.muon_check_finite(g.plan, grads, 5, flag, ws, ws_bytes, 0)
+    assert ei.value.name == "MUON_ERR_INVALID_ARG"
+    with pytest.raises(M.MuonError) as ei:
+        M.muon_check_finite(g.plan, grads, "fp32", 0, ws, ws_bytes, 0)
+    assert ei.value.name == "MUON_ERR_INVALID_ARG"
+    with pytest.raises(M.MuonError) as ei:
+        M.muon_check_finite(g.plan, grads, "fp32", grads[0] + 8, ws, ws_bytes, 0)
+    assert ei.value.name == "MUON_ERR_ALIAS"
+    # apply: no step has run on this workspace yet
+    with pytest.raises(M.MuonError) as ei:
+        M.muon_apply_update(g.plan, params, parts, 0.1, 0.0, 1.0, None, None, ws, ws_bytes, 0)
+    assert ei.value.name == "MUON_ERR_INVALID_ARG"
+    assert "no muon_step" in str(ei.value)
+    # non-finite hyper-parameters, NULL entries
+    with pytest.raises(M.MuonError) as ei:
+        M.muon_apply_update(g.plan, params, parts, float("nan"), 0.0, 1.0, None, None, ws, ws_bytes, 0)
+    assert ei.value.name == "MUON_ERR_INVALID_ARG"
+    with pytest.raises(M.MuonError) as ei:
+        M.muon_apply_update(g.plan, [0], parts, 0.1, 0.0, 1.0, None, None, ws, ws_bytes, 0)
+    assert ei.value.name == "MUON_ERR_INVALID_ARG"
