@@ -262,6 +262,20 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # the step after the path (update norm, clipping, parameter update on
+    # fp32 master partitions), timed on its own after the timed steps
+    params_flat = torch.zeros(wl.num_partitions * P, dtype=torch.float32, device="cuda:0")
+    params = [params_flat[r * P:(r + 1) * P] for r in range(wl.num_partitions)]
+    apply_ms = []
+    for i in range(1 + args.steps):
+        ev0.record()
+        g.apply_update(params, parts, 1e-3, 0.1, 1.0, ws)
+        ev1.record()
+        torch.cuda.synchronize()
+        if i:
+            apply_ms.append(ev0.elapsed_time(ev1))
+    del params, params_flat
+
     probs = g.problems()
     nom, sym = ns_flops(probs, method, g.options.ns_steps)
     k1_ms = statistics.mean(p[0] for p in phases)
@@ -295,12 +309,15 @@ def main() -> int:
                    "partitions": wl.num_partitions, "ns_method": method, "ns_steps": g.options.ns_steps,
                    "ns_precision": args.precision, "grad_dtype": step_dtype},
         "phases_ms": {"k1_norm": round(k1_ms, 3), "newton_schulz": round(ns_ms, 3), "k3_scatter": round(k3_ms, 3),
-                      "accumulate": round(statistics.mean(acc_ms), 3) if acc is not None else None},
+                      "accumulate": round(statistics.mean(acc_ms), 3) if acc is not None else None,
+                      "apply_update": round(statistics.mean(apply_ms), 3)},
         "ns_tflops_nominal": round(ns_tflops_nom, 1),
         "ns_pct_peak_nominal": round(100 * ns_tflops_nom / peak, 2),
         "k1_gbs": round(k1_bytes / (k1_ms * 1e-3) / 1e9, 1),
         "k3_gbs": round(k3_bytes / (k3_ms * 1e-3) / 1e9, 1),
         "accumulate_gbs": round(acc_bytes / (statistics.mean(acc_ms) * 1e-3) / 1e9, 1) if acc is not None else None,
+        # read p, read u, write p: 12 B per owned element
+        "apply_gbs": round(numel * 12 / (statistics.mean(apply_ms) * 1e-3) / 1e9, 1),
         "roofline": {"kernel": "ns_gemm (grouped Newton-Schulz GEMM)", "bound": "mfma",
                      "achieved": round(ns_tflops_sym, 1), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(ns_tflops_sym / peak, 4), "traffic": measured_traffic(wl.name),
