@@ -405,7 +405,8 @@ muon_status muon_apply_update(muon_plan *p, float *const *params, const float *c
   char *wsb = static_cast<char *>(ws);
   const float *nparts = reinterpret_cast<const float *>(wsb + p->nparts_off);
   float *nc = reinterpret_cast<float *>(wsb + p->nc_off);
-  hipError_t e = launch_norm_clip(nparts, p->nparts_n, max_norm, nc, norm_clip_out, skip_flag, s);
+  double *l1 = reinterpret_cast<double *>(wsb + p->nl1_off);
+  hipError_t e = launch_norm_clip(nparts, p->nparts_n, l1, max_norm, nc, norm_clip_out, skip_flag, s);
   if (e != hipSuccess) return hip_fail(e, "norm launch");
   e = launch_apply(static_cast<const KARun *>(ws), (int)tab.size(), ch, nc, lr, weight_decay, skip_flag, s);
   if (e != hipSuccess) return hip_fail(e, "apply launch");

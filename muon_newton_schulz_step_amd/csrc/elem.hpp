@@ -22,10 +22,12 @@ hipError_t launch_kc(const ProbDev *probs, const K1Prob *k1, int nprob, char *ws
                      const int32_t *skip, hipStream_t s);
 // flag = 1 if any element of the matrices is not finite, else 0
 hipError_t launch_finite(const K0Mat *mats, int nmat, int64_t chunks, bool gbf16, int32_t *flag, hipStream_t s);
-// norm = sqrt(sum of nparts[0..n)) (fp64, fixed order); nc[0] = norm,
-// nc[1] = clip factor; copied to user_out[0..2) when that is not NULL
-hipError_t launch_norm_clip(const float *nparts, int64_t n, float max_norm, float *nc, float *user_out,
+// norm = sqrt(sum of nparts[0..n)) (fp64, fixed order, through l1: one
+// double per 8192 partials); nc[0] = norm, nc[1] = clip factor; copied to
+// user_out[0..2) when that is not NULL
+hipError_t launch_norm_clip(const float *nparts, int64_t n, double *l1, float max_norm, float *nc, float *user_out,
                             const int32_t *skip, hipStream_t s);
+constexpr int64_t kNormSpan = 8192;  // partials per level-1 sum
 // param = param * (1 - lr wd) - (lr clip) upd on every run
 hipError_t launch_apply(const KARun *runs, int nrun, int64_t chunks, const float *nc, float lr, float wd,
                         const int32_t *skip, hipStream_t s);

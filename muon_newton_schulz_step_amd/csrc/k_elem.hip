@@ -341,20 +341,40 @@ __global__ __launch_bounds__(256) void kf_scan(const K0Mat *mats, int nmat, int3
 
 // ----------------------------------------------------------------- norm, clip, apply
 
-__global__ __launch_bounds__(256) void k_norm_clip(const float *nparts, int64_t n, float max_norm, float *nc,
-                                                   float *user_out, const int32_t *skip) {
-  if (skip && *skip) return;
+// Two-level fixed-order sum of the writeback's chunk partials: level 1 sums
+// kNormSpan consecutive partials per workgroup, level 2 (one workgroup)
+// sums the level-1 results, both in fp64 with a fixed thread / tree order.
+
+__device__ __forceinline__ double block_sum_f64(double s) {
   __shared__ double red[256];
-  double s = 0.0;
-  for (int64_t i = threadIdx.x; i < n; i += 256) s += (double)nparts[i];
   red[threadIdx.x] = s;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
     if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
     __syncthreads();
   }
+  return red[0];
+}
+
+__global__ __launch_bounds__(256) void k_norm_level1(const float *nparts, int64_t n, double *l1,
+                                                     const int32_t *skip) {
+  if (skip && *skip) return;
+  const int64_t b = (int64_t)blockIdx.x * kNormSpan;
+  const int64_t e = min(b + (int64_t)kNormSpan, n);
+  double s = 0.0;
+  for (int64_t i = b + threadIdx.x; i < e; i += 256) s += (double)nparts[i];
+  const double t = block_sum_f64(s);
+  if (threadIdx.x == 0) l1[blockIdx.x] = t;
+}
+
+__global__ __launch_bounds__(256) void k_norm_clip(const double *l1, int n1, float max_norm, float *nc,
+                                                   float *user_out, const int32_t *skip) {
+  if (skip && *skip) return;
+  double s = 0.0;
+  for (int i = threadIdx.x; i < n1; i += 256) s += l1[i];
+  const double tot = block_sum_f64(s);
   if (threadIdx.x == 0) {
-    const double norm = sqrt(red[0]);
+    const double norm = sqrt(tot);
     double clip = 1.0;
     if (max_norm > 0.f) clip = fmin(1.0, (double)max_norm / (norm + 1e-6));
     nc[0] = (float)norm;
@@ -463,9 +483,15 @@ hipError_t launch_finite(const K0Mat *mats, int nmat, int64_t chunks, bool gbf16
   return hipGetLastError();
 }
 
-hipError_t launch_norm_clip(const float *nparts, int64_t n, float max_norm, float *nc, float *user_out,
+hipError_t launch_norm_clip(const float *nparts, int64_t n, double *l1, float max_norm, float *nc, float *user_out,
                             const int32_t *skip, hipStream_t s) {
-  hipLaunchKernelGGL(k_norm_clip, dim3(1), dim3(256), 0, s, nparts, n, max_norm, nc, user_out, skip);
+  const int n1 = (int)((n + kNormSpan - 1) / kNormSpan);
+  if (n1 > 0) {
+    hipLaunchKernelGGL(k_norm_level1, dim3((unsigned)n1), dim3(256), 0, s, nparts, n, l1, skip);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_norm_clip, dim3(1), dim3(256), 0, s, l1, n1, max_norm, nc, user_out, skip);
   return hipGetLastError();
 }
 

@@ -1,4 +1,5 @@
 // Host planner (no HIP calls).  See plan.hpp.
+#include "elem.hpp"
 #include "plan.hpp"
 
 #include <algorithm>
@@ -450,6 +451,7 @@ muon_status build_plan(muon_plan *p) {
   p->nparts_n = nparts;
   p->nparts_off = ws.take(std::max<int64_t>(nparts, 1) * 4);
   p->nc_off = ws.take(2 * 4);
+  p->nl1_off = ws.take(std::max<int64_t>((nparts + kNormSpan - 1) / kNormSpan, 1) * 8);
   p->data_off = ws.take(max_data);
   p->ws_bytes = rup(ws.top, kAlign);
   // absolute offsets inside the workspace

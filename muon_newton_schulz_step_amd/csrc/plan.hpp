@@ -82,7 +82,7 @@ struct muon_plan {
   int64_t max_k1_tiles = 0, max_probs = 0;
   int64_t k0_table_bytes = 0;  // accumulation table (shares the table region)
   // update norm: per-K3-chunk sums of squares (all waves), then [norm, clip]
-  int64_t nparts_off = 0, nparts_n = 0, nc_off = 0;
+  int64_t nparts_off = 0, nparts_n = 0, nc_off = 0, nl1_off = 0;
   const void *norm_ws = nullptr;  // workspace of the last muon_step (its partials are current)
   std::vector<char> host_tables;  // serialized tables (pointers patched per call)
   // lazily created HIP resources (pinned staging, events), see abi.cpp
