@@ -144,3 +144,22 @@ def test_llama7b_full_group_sampled(torch):
     _finite_and_covered(torch, parts_flat, wl, offsets)
     st = g.stats()
     assert st["ns_invocations"] == 224 and st["accumulations"] == 4 and st["steps"] == 1
+
+
+def test_share70b_full_group_sampled(torch):
+    """The 70B single-GPU share (8 layers, 56 matrices, 6.85 G elements) in
+    the bench's launch configuration.  The oracle checks the k and v
+    projections (8192 x 1024, tall: 1024 x 8192 blocks on the large-tile
+    kernel, shape scale 2.83) of the first and last layer; the 8192-wide
+    matrices would take the fp64 oracle minutes each, so every matrix of the
+    group gets the size-independent checks instead."""
+    wl = W.share70b()
+    L = len(wl.shapes)
+    sample = [1, 2, L - 5]                # layer 0 k, v; layer 7 k
+    got, want, parts_flat, offsets, P, g = _run_group(torch, wl, "standard", sample)
+    for i in sample:
+        err = O.rel_frobenius(got[i], want[i])
+        print(f"70B share, matrix {i} {wl.shapes[i]}: rel err {err:.3e}")
+        assert err <= TOL_BF16
+    _finite_and_covered(torch, parts_flat, wl, offsets)
+    assert g.stats()["ns_invocations"] == L
