@@ -68,8 +68,139 @@ __device__ __forceinline__ uint4 mask_tail(uint4 v, int valid) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+// store n (<= 8) bf16 values packed in w at dst: one 16-byte store when
+// whole and aligned, element stores otherwise
+__device__ __forceinline__ void store8(uint16_t *dst, uint4 w, int n) {
+  if (n == 8 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+    *reinterpret_cast<uint4 *>(dst) = w;
+  } else {
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    for (int e = 0; e < n; ++e) dst[e] = (uint16_t)(ww[e >> 1] >> (16 * (e & 1)));
+  }
+}
+
+// Epilogue for bf16 outputs (and, if any, a bf16 symmetric D): the
+// accumulators are transformed in registers (D read as D[col][row .. row+3],
+// which its symmetry allows), staged once as bf16 in column-major order
+// (column stride 264 bytes) behind one barrier, then stored 16 bytes per
+// lane: row-major outputs gathered with transposing LDS reads
+// (ds_read_b64_tr_b16: lane i of a 16-lane group receives element (i % 4) of
+// the 8 bytes lane 4 e + i / 4 addresses, for e = 0..3), transposed and
+// mirror outputs with contiguous reads.
+constexpr int SCB = 264;
+__device__ __forceinline__ void staged_epilogue(const GemmArgs &args, const GemmRecipe &R, const ProbDev &P,
+                                                const TileDev &tile, const f32x16 (&acc)[2][2], float sc,
+                                                bool mirror, bool t0, bool t1, bool diag, const char *D,
+                                                int64_t ldd, char *S0, int64_t ld0, char *S1, int64_t ld1,
+                                                int64_t M, int64_t N, int64_t m0, int64_t n0, char *lds) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 31, lg = lane >> 5;
+  const int64_t col0 = n0 + wn * 64 + lr;       // + 32 j
+  const int64_t row0 = m0 + wm * 64 + 4 * lg;   // + 32 i + 8 g
+  uint2 dq[2][2][4];
+  if (D) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t gj = col0 + 32 * j, gi = row0 + 32 * i + 8 * g;
+          uint2 w = make_uint2(0, 0);
+          // rows gi .. gi+3 may run past M only where nothing is stored
+          if (gj < N && gi < M) w = *reinterpret_cast<const uint2 *>(D + (gj * ldd + gi) * 2);
+          dq[i][j][g] = w;
+        }
+  }
+  __syncthreads();  // every wave is done with the stage buffers
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t gi = row0 + 32 * i + 8 * g, gj = col0 + 32 * j;
+        float d[4] = {0.f, 0.f, 0.f, 0.f};
+        if (D) {
+          const uint2 w = dq[i][j][g];
+          d[0] = __uint_as_float(w.x << 16); d[1] = __uint_as_float(w.x & 0xffff0000u);
+          d[2] = __uint_as_float(w.y << 16); d[3] = __uint_as_float(w.y & 0xffff0000u);
+        }
+        uint16_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float x = acc[i][j][4 * g + e] * R.cacc;
+          if (D) x = fmaf(R.cd, d[e], x);
+          x *= sc;
+          if (diag && gi + e == gj) x += R.cdiag;
+          h[e] = f2bf(x);
+        }
+        const int cl = wn * 64 + 32 * j + lr, rl = wm * 64 + 32 * i + 8 * g + 4 * lg;
+        *reinterpret_cast<uint2 *>(lds + cl * SCB + rl * 2) =
+            make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+      }
+  __syncthreads();
+  const bool r0 = !t0, r1 = S1 && !t1, c0 = t0 || mirror, c1 = S1 && (t1 || mirror);
+  char *rowA = r0 ? S0 : S1, *rowB = S1;
+  const int64_t rowLA = r0 ? ld0 : ld1, rowLB = ld1;
+  const int nrow = (int)r0 + (int)r1;
+  char *colA = c0 ? S0 : S1, *colB = S1;
+  const int64_t colLA = c0 ? ld0 : ld1, colLB = ld1;
+  const int ncol = (int)c0 + (int)c1;
+  if (nrow) {
+    // 16-lane group q4 of wave w, step it: rows rb .. rb+16 with
+    // rb = 16 (4 (it / 4) + w), columns cb .. cb+8 with cb = 32 (it % 4) +
+    // 8 q4; lane li supplies column cb + li/4 (and +4), rows rb + 4 (li % 4)
+    // .. +3, and ends up with columns cb .. cb+7 of row rb + li
+    const int q4 = lane >> 4, li = lane & 15;
+#pragma unroll 2
+    for (int it = 0; it < 8; ++it) {
+      const int rb = 16 * (4 * (it >> 2) + wave);
+      const int cb = 32 * (it & 3) + 8 * q4;
+      const char *base = lds + (cb + (li >> 2)) * SCB + (rb + 4 * (li & 3)) * 2;
+      const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(base));
+      const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(base + 4 * SCB));
+      // the reads exchange data across the 16 lanes of a group: keep them
+      // ahead of the per-lane branch below, with every lane active
+      asm volatile("" ::"v"(lo4), "v"(hi4));
+      const int64_t gi = m0 + rb + li, gj = n0 + cb;
+      if (gi >= M || gj >= N) continue;
+      const uint4 w = make_uint4((uint32_t)(uint16_t)lo4[0] | ((uint32_t)(uint16_t)lo4[1] << 16),
+                                 (uint32_t)(uint16_t)lo4[2] | ((uint32_t)(uint16_t)lo4[3] << 16),
+                                 (uint32_t)(uint16_t)hi4[0] | ((uint32_t)(uint16_t)hi4[1] << 16),
+                                 (uint32_t)(uint16_t)hi4[2] | ((uint32_t)(uint16_t)hi4[3] << 16));
+      const int nv = (int)min<int64_t>(N - gj, 8);
+      store8(reinterpret_cast<uint16_t *>(rowA) + gi * rowLA + gj, w, nv);
+      if (nrow > 1) store8(reinterpret_cast<uint16_t *>(rowB) + gi * rowLB + gj, w, nv);
+    }
+  }
+  if (ncol) {
+    // 16 lanes per column: column c, rows 8 (lane % 16) .. +8
+#pragma unroll 2
+    for (int it = 0; it < 8; ++it) {
+      const int c = 4 * (4 * it + wave) + (lane >> 4);
+      const int r8 = 8 * (lane & 15);
+      const char *src = lds + c * SCB + r8 * 2;
+      const uint2 a2 = *reinterpret_cast<const uint2 *>(src);
+      const uint2 b2 = *reinterpret_cast<const uint2 *>(src + 8);
+      const int64_t gj = n0 + c, gi = m0 + r8;
+      if (gj >= N || gi >= M) continue;
+      const uint4 w = make_uint4(a2.x, a2.y, b2.x, b2.y);
+      const int nv = (int)min<int64_t>(M - gi, 8);
+      store8(reinterpret_cast<uint16_t *>(colA) + gj * colLA + gi, w, nv);
+      if (ncol > 1) store8(reinterpret_cast<uint16_t *>(colB) + gj * colLB + gi, w, nv);
+    }
+  }
+  (void)args; (void)P; (void)tile;
+}
+
 template <bool BF16>
-__global__ __launch_bounds__(NTHR) void ns_gemm(GemmArgs args) {
+__global__ __launch_bounds__(NTHR, 3) void ns_gemm(GemmArgs args) {
   if (args.skip && *args.skip) return;
   constexpr int ES = BF16 ? 2 : 4;   // operand element bytes
   constexpr int BK = 64 / ES;        // K elements per staged row
@@ -192,6 +323,11 @@ __global__ __launch_bounds__(NTHR) void ns_gemm(GemmArgs args) {
   const int64_t ld0 = P.ld[R.rS0];
   char *S1 = R.rS1 >= 0 ? args.ws + P.off[R.rS1] : nullptr;
   const int64_t ld1 = R.rS1 >= 0 ? P.ld[R.rS1] : 0;
+  if (!f0 && (!S1 || !f1) && (!D || (!fd && (R.flags & GF_SYM)))) {
+    staged_epilogue(args, R, P, tile, acc, sc, mirror, t0, t1, diag, D, ldd, S0, ld0, S1, ld1, M, N, m0, n0,
+                    &lds[0][0][0]);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
