@@ -96,8 +96,10 @@ def _views(flat, shapes):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ns_gemm_llama7b_32layer_hbm_traffic.md")
-TRAFFIC_SOURCES = ("muon_newton_schulz_step_amd/csrc/k_gemm256.hip", "muon_newton_schulz_step_amd/csrc/k_gemm.hip",
-                   "muon_newton_schulz_step_amd/csrc/plan.cpp")
+# the sources behind the Llama-7B group's Newton-Schulz launches (all of its
+# blocks are 4096 wide, so they run on the large-tile kernel only)
+TRAFFIC_SOURCES = ("muon_newton_schulz_step_amd/csrc/k_gemm256.hip", "muon_newton_schulz_step_amd/csrc/plan.cpp",
+                   "muon_newton_schulz_step_amd/csrc/tables.hpp")
 
 
 def measured_traffic(workload: str):
