@@ -126,11 +126,13 @@ def measured_traffic(workload: str):
         return None
 
 
-def cpu_baseline(wl, method: str, total_nominal: float, budget_s: float):
-    """The oracle (fp64 numpy, as it stands) on a bounded sample: the first
-    matrix of the group run through the whole step (momentum, Newton-Schulz,
-    shape scale, writeback), extrapolated to the group by nominal
-    Newton-Schulz flops."""
+def cpu_baseline(wl, method: str, budget_s: float):
+    """The oracle (fp64 numpy, as it stands) on a bounded sample: one matrix
+    of each distinct kind (shape and head count) run through the whole step
+    (momentum, Newton-Schulz, shape scale, writeback), smallest kinds first,
+    while the measured time stays within the budget.  The group time is the
+    sum over kinds of count x measured time; kinds left untimed are
+    extrapolated by nominal Newton-Schulz flops at the measured rate."""
     import numpy as np
     import oracle.muon_oracle as O
     import workloads as W
@@ -139,39 +141,42 @@ def cpu_baseline(wl, method: str, total_nominal: float, budget_s: float):
         threads = max([t.get("num_threads", 1) for t in threadpool_info() if t.get("user_api") == "blas"] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    # pick the largest matrix kind whose estimated fp64 time fits the budget
-    shapes = sorted(set(wl.shapes), key=lambda s: s[0] * s[1])
+
+    def nominal(s, h):
+        h = h or 1
+        m, n = min(s[0] // h, s[1]), max(s[0] // h, s[1])
+        return h * (5 * (4 * m * m * n + 2 * m ** 3) if method == "standard" else 4 * m * m * n + 34 * m ** 3)
+
+    kinds = {}
+    for s, h in zip(wl.shapes, wl.heads):
+        kinds[(s, h)] = kinds.get((s, h), 0) + 1
+    order = sorted(kinds, key=lambda k: nominal(*k))
     probe = O.ns_standard(W.gaussian((512, 512), 1, 1.0).astype(np.float64) / 512.0)  # warm the BLAS
     del probe
-    t0 = time.perf_counter()
-    x = W.gaussian((1024, 1024), 2, 1.0).astype(np.float64)
-    _ = x @ x
-    gflops = 2 * 1024 ** 3 / (time.perf_counter() - t0) / 1e9
-    pick = shapes[0]
-    heads = 0
-    for s in shapes:
-        i = wl.shapes.index(s)
-        h = wl.heads[i] or 1
-        m, n = min(s[0] // h, s[1]), max(s[0] // h, s[1])
-        f = h * (5 * (4 * m * m * n + 2 * m ** 3) if method == "standard" else 4 * m * m * n + 34 * m ** 3)
-        if f / (gflops * 1e9) <= budget_s:
-            pick, heads = s, wl.heads[i]
-    r, c = pick
-    h = heads or 1
-    m, n = min(r // h, c), max(r // h, c)
-    sample_flops = h * (5 * (4 * m * m * n + 2 * m ** 3) if method == "standard" else 4 * m * m * n + 34 * m ** 3)
-    g = W.gaussian(pick, 12345, wl.sigma).astype(np.float64)
-    state = O.init_state([pick])
-    offsets, P = O.pack_layout([pick], 1, 16)
-    t0 = time.perf_counter()
-    O.muon_step([g], state, [pick], [heads], offsets, 1, P, O.MuonOptions(method=method))
-    dt = time.perf_counter() - t0
-    ms = dt * 1e3 * total_nominal / sample_flops
-    return {"value": round(ms, 1), "unit": "ms", "cores": int(threads), "kind": "oracle",
-            "sample": (f"one {r}x{c} matrix{' (%d heads)' % heads if heads else ''} through the oracle step "
-                       f"(fp64 numpy) in {dt:.2f} s, extrapolated to the {len(wl.shapes)}-matrix group by "
-                       f"nominal Newton-Schulz flops ({sample_flops / 1e12:.3f} of {total_nominal / 1e12:.1f} TFLOP)"),
-            "extrapolated": True}
+    timed, spent, rate = [], 0.0, None
+    for (s, h) in order:
+        f = nominal(s, h)
+        if rate is not None and spent + f / rate > budget_s:
+            break
+        g = W.gaussian(s, 12345, wl.sigma).astype(np.float64)
+        state = O.init_state([s])
+        offsets, P = O.pack_layout([s], 1, 16)
+        t0 = time.perf_counter()
+        O.muon_step([g], state, [s], [h], offsets, 1, P, O.MuonOptions(method=method))
+        dt = time.perf_counter() - t0
+        spent += dt
+        timed.append(((s, h), dt))
+        rate = sum(nominal(*k) for k, _ in timed) / spent
+        if spent > budget_s:
+            break
+    done = {k for k, _ in timed}
+    total_s = sum(kinds[k] * dt for k, dt in timed) + sum(kinds[k] * nominal(*k) / rate for k in kinds if k not in done)
+    desc = ", ".join(f"{s[0]}x{s[1]}{'/%dh' % h if h else ''} ({dt:.2f} s)" for (s, h), dt in timed)
+    return {"value": round(total_s * 1e3, 1), "unit": "ms", "cores": int(threads), "kind": "oracle",
+            "sample": (f"one matrix of each kind through the oracle step (fp64 numpy): {desc}; the group time is "
+                       f"count x time per kind" + ("" if len(done) == len(kinds) else
+                                                     ", untimed kinds extrapolated by nominal flops")),
+            "extrapolated": len(done) != len(kinds)}
 
 
 def main() -> int:
@@ -329,7 +334,7 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample")
-        line["cpu_baseline"] = cpu_baseline(wl, method, nom, args.cpu_budget_s)
+        line["cpu_baseline"] = cpu_baseline(wl, method, args.cpu_budget_s)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
