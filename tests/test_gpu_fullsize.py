@@ -135,7 +135,9 @@ def test_per_head_gram_full_group_sampled(torch):
 
 def test_llama7b_full_group_sampled(torch):
     wl = W.llama7b()
-    sample = [0, len(wl.shapes) - 1]      # layer 0 q (4096x4096), layer 31 down (11008x4096, shape scale)
+    # every matrix kind: layer 0 q (4096x4096) and gate (4096x11008), layer 31
+    # down (11008x4096, transposed, shape scale)
+    sample = [0, 4, len(wl.shapes) - 1]
     got, want, parts_flat, offsets, P, g = _run_group(torch, wl, "standard", sample)
     for i in sample:
         err = O.rel_frobenius(got[i], want[i])
