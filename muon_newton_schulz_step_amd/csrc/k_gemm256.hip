@@ -11,8 +11,12 @@
 //  - K staged 64 deep (128-byte rows) straight from global memory into LDS
 //    with 16-byte LDS-DMA loads (global_load_lds_dwordx4: lane L lands at
 //    base + 16 L), double buffered: the loads of stage t+1 are in flight
-//    while stage t feeds the MFMAs.  A ragged last stage (K not a multiple
-//    of 64) goes through registers so elements at k >= K are zeroed.
+//    while stage t feeds the MFMAs.  The 16 DMA instructions of a stage are
+//    issued one per MFMA pair across two k-steps; issued back to back they
+//    stall the wave (and its MFMAs) until the address unit drains them,
+//    which cost a third of the main loop.  A ragged last stage (K not a
+//    multiple of 64) goes through registers so elements at k >= K are
+//    zeroed.
 //  - 16-byte chunks of each row are XOR-swizzled (position = chunk ^ f(row))
 //    so the 32 rows a fragment read touches spread over all LDS banks.
 //  - Workgroup i runs on XCD i mod 8; the tile list (ordered in 4 x 8
@@ -329,74 +333,84 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
     }
   };
   if (nfull == nk) {
-    // K a multiple of 64: every stage is a whole LDS-DMA stage, issued
-    // without branches so that its 16 instructions interleave with the
-    // MFMAs of the step that follows the barrier.  The destination rows of
-    // this wave are uniform, so M0 is computed on the scalar unit.
+    // K a multiple of 64: every stage is a whole LDS-DMA stage.  The 16
+    // DMA instructions of stage t+2 are spread over two k-steps (one per
+    // MFMA pair): the A rows over the k-step after the barrier that frees
+    // the buffer, the B rows over the first k-step of the next stage.  A
+    // burst of 16 would hold up the wave's MFMAs until the address unit
+    // drains it.  The destination rows of this wave are uniform, so M0 is
+    // computed on the scalar unit.
     const int wv = __builtin_amdgcn_readfirstlane(wave);
-    auto dma = [&](int kt, int st) {
+    auto dma1 = [&](int kt, int st, int q) {
       const int seg = !SPLIT ? 0 : (kt >= nk ? (kt >= 2 * nk ? 2 : 1) : 0);
       const int64_t k0 = (int64_t)(kt - seg * nk) * KS;
-      const char *a = A + (seg == 0 ? 0 : (seg == 1 ? dA1 : dA2));
-      const char *b = B + (seg == 0 ? 0 : (seg == 1 ? dB1 : dB2));
       char *la = lds + st * 2 * OPB + wv * 64 * ROWB;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      const int j = q & 7;
+      if (q < 8) {
+        const char *a = A + (seg == 0 ? 0 : (seg == 1 ? dA1 : dA2));
         __builtin_amdgcn_global_load_lds(a + (arow[j] + k0 + lchunk[j]) * 2, (lds_void *)(la + j * 8 * ROWB), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(b + (brow[j] + k0 + lchunk[j]) * 2, (lds_void *)(la + OPB + j * 8 * ROWB), 16,
-                                         0, 0);
+      } else {
+        const char *b = B + (seg == 0 ? 0 : (seg == 1 ? dB1 : dB2));
+        __builtin_amdgcn_global_load_lds(b + (brow[j] + k0 + lchunk[j]) * 2, (lds_void *)(la + OPB + j * 8 * ROWB),
+                                         16, 0, 0);
       }
     };
-    auto interleave_dma = [&]() {
-      // 16 MFMAs with the 16 LDS-DMA instructions and 8 fragment reads
+    // fragment read q of a k-step, in the order the next step's MFMA pairs
+    // consume them: A0, B0, B1, B2, B3, A1, A2, A3
+    auto read1 = [&](int set, int st, int ks, int q) {
+      const char *la = lds + st * 2 * OPB;
+      const char *lb = la + OPB;
+      const int c = ks * 2 + lg;
+      if (q == 0) fa[set][0] = *reinterpret_cast<const bf16x8_t *>(la + arb[0] + swz(ak[0], c) * 16);
+      else if (q <= 4) fb[set][q - 1] = *reinterpret_cast<const bf16x8_t *>(lb + brb[q - 1] + swz(bk[q - 1], c) * 16);
+      else fa[set][q - 4] = *reinterpret_cast<const bf16x8_t *>(la + arb[q - 4] + swz(ak[q - 4], c) * 16);
+    };
+    // one 16-deep k-step on fragment set `set`, in eight groups of an MFMA
+    // pair, one fragment read of the next step (RD) and one DMA instruction
+    // (DMA: instructions q0 .. q0 + 7 of stage dkt into buffer dst); the
+    // groups keep their order
+    auto kstep = [&](int set, auto rd_, int rst, int rks, auto dma_, int dkt, int dst, int q0) {
+      constexpr bool RD = decltype(rd_)::value;
+      constexpr bool DMA = decltype(dma_)::value;
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x010, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        const int i = n >> 1, j = (n & 1) * 2;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
+        acc[i][j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j + 1], acc[i][j + 1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (RD) {
+          // the fragment reads of the next step finish two MFMA pairs
+          // before it starts (the wait there covers every outstanding read)
+          if (n < 2) { read1(set ^ 1, rst, rks, 2 * n); read1(set ^ 1, rst, rks, 2 * n + 1); }
+          else if (n < 6) read1(set ^ 1, rst, rks, n + 2);
+        }
+        if constexpr (DMA) dma1(dkt, dst, q0 + n);
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
-    dma(0, 0);
+    constexpr std::true_type yes{};
+    constexpr std::false_type no{};
+#pragma unroll
+    for (int q = 0; q < 16; ++q) dma1(0, 0, q);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (nkt > 1) dma(1, 1);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) dma1(min(1, nkt - 1), 1, q);
     read_frags(0, 0, 0);
-    int kt = 0;
-    for (; kt + 2 < nkt; ++kt) {
+    // One loop body for every stage: past the end, the DMA stage index is
+    // clamped to the last stage, which reloads data into a buffer nobody
+    // reads again (the epilogue waits for those loads before reusing LDS).
+    for (int kt = 0; kt < nkt; ++kt) {
       const int st = kt & 1;
-      read_frags(1, st, 1);
-      mfmas(0);
-      interleave();
-      read_frags(0, st, 2);
-      mfmas(1);
-      interleave();
-      read_frags(1, st, 3);
-      mfmas(0);
-      interleave();
+      kstep(0, yes, st, 1, yes, min(kt + 1, nkt - 1), st ^ 1, 8);   // B rows of stage kt+1
+      kstep(1, yes, st, 2, no, 0, 0, 0);
+      kstep(0, yes, st, 3, no, 0, 0, 0);
+      // stage kt+1 landed and every wave is done reading stage kt
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      dma(kt + 2, st);
-      read_frags(0, st ^ 1, 0);
-      mfmas(1);
-      interleave_dma();
+      kstep(1, yes, st ^ 1, 0, yes, min(kt + 2, nkt - 1), st, 0);   // A rows of stage kt+2
     }
-    for (; kt < nkt; ++kt) {            // the last two stages: nothing left to load
-      const int st = kt & 1;
-      read_frags(1, st, 1);
-      mfmas(0);
-      interleave();
-      read_frags(0, st, 2);
-      mfmas(1);
-      interleave();
-      read_frags(1, st, 3);
-      mfmas(0);
-      interleave();
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (kt + 1 < nkt) read_frags(0, st ^ 1, 0);
-      mfmas(1);
-      interleave();
-    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   } else {
   stage(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
