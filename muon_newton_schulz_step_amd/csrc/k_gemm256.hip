@@ -71,12 +71,13 @@ __device__ __forceinline__ int swz(int r, int c) {
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t b = __float_as_uint(f);
-  if ((b & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((b >> 16) | 0x40u);
-  b += 0x7fffu + ((b >> 16) & 1u);
-  return (uint16_t)(b >> 16);
+// round to nearest even (v_cvt_pk_bf16_f32)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk2(float a, float b) {
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
+__device__ __forceinline__ uint16_t f2bf(float f) { return (uint16_t)pk2(f, 0.f); }
 
 __device__ __forceinline__ void store_elem(char *base, int64_t idx, float v, bool f32) {
   if (f32) reinterpret_cast<float *>(base)[idx] = v;
@@ -165,21 +166,28 @@ __device__ __forceinline__ void unpack8(const uint4 w, float *v) {
   }
 }
 __device__ __forceinline__ uint4 pack8(const float *v) {
-  uint4 w;
-  w.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-  w.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-  w.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
-  w.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
-  return w;
+  return make_uint4(pk2(v[0], v[1]), pk2(v[2], v[3]), pk2(v[4], v[5]), pk2(v[6], v[7]));
+}
+
+// 16-byte nontemporal store (the outputs are read back by the next launch,
+// long after they would have left the L2)
+__device__ __forceinline__ void st16(char *p, uint4 v) {
+  __builtin_nontemporal_store(v.x, reinterpret_cast<uint32_t *>(p));
+  __builtin_nontemporal_store(v.y, reinterpret_cast<uint32_t *>(p) + 1);
+  __builtin_nontemporal_store(v.z, reinterpret_cast<uint32_t *>(p) + 2);
+  __builtin_nontemporal_store(v.w, reinterpret_cast<uint32_t *>(p) + 3);
 }
 
 // hi = the bf16 value nearest v, lo = v - hi (then rounded to bf16 when
 // stored): hi + lo carries about 16 significant bits of v
 __device__ __forceinline__ void split4(const float *v, float *hi, float *lo) {
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    hi[e] = bf2f(f2bf(v[e]));
+  for (int e = 0; e < 4; e += 2) {
+    const uint32_t h = pk2(v[e], v[e + 1]);
+    hi[e] = __uint_as_float(h << 16);
+    hi[e + 1] = __uint_as_float(h & 0xffff0000u);
     lo[e] = v[e] - hi[e];
+    lo[e + 1] = v[e + 1] - hi[e + 1];
   }
 }
 
@@ -561,12 +569,12 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
           split4(v, hi, lo);
           split4(v + 4, hi + 4, lo + 4);
           if (!t0) {
-            *reinterpret_cast<uint4 *>(S0 + (gi * ld0 + gj) * 2) = pack8(hi);
-            *reinterpret_cast<uint4 *>(S1 + (gi * ld1 + gj) * 2) = pack8(lo);
+            st16(S0 + (gi * ld0 + gj) * 2, pack8(hi));
+            st16(S1 + (gi * ld1 + gj) * 2, pack8(lo));
           }
         } else {
-          if (!t0) *reinterpret_cast<uint4 *>(S0 + (gi * ld0 + gj) * 2) = pack8(v);
-          if (S1 && !t1) *reinterpret_cast<uint4 *>(S1 + (gi * ld1 + gj) * 2) = pack8(v);
+          if (!t0) st16(S0 + (gi * ld0 + gj) * 2, pack8(v));
+          if (S1 && !t1) st16(S1 + (gi * ld1 + gj) * 2, pack8(v));
         }
       }
     };
@@ -641,12 +649,12 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
           split4(v, hi, lo);
           split4(v + 4, hi + 4, lo + 4);
           if (t0 || mirror) {
-            *reinterpret_cast<uint4 *>(S0 + (gj * ld0 + gi) * 2) = pack8(hi);
-            *reinterpret_cast<uint4 *>(S1 + (gj * ld1 + gi) * 2) = pack8(lo);
+            st16(S0 + (gj * ld0 + gi) * 2, pack8(hi));
+            st16(S1 + (gj * ld1 + gi) * 2, pack8(lo));
           }
         } else {
-          if (t0 || mirror) *reinterpret_cast<uint4 *>(S0 + (gj * ld0 + gi) * 2) = pack8(v);
-          if (S1 && (t1 || mirror)) *reinterpret_cast<uint4 *>(S1 + (gj * ld1 + gi) * 2) = pack8(v);
+          if (t0 || mirror) st16(S0 + (gj * ld0 + gi) * 2, pack8(v));
+          if (S1 && (t1 || mirror)) st16(S1 + (gj * ld1 + gi) * 2, pack8(v));
         }
       }
     } else if (col_phase) {
