@@ -36,11 +36,11 @@ constexpr int NTHR = 256;
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32; NaN stays NaN)
 __device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t b = __float_as_uint(f);
-  if ((b & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((b >> 16) | 0x40u);
-  b += 0x7fffu + ((b >> 16) & 1u);
-  return (uint16_t)(b >> 16);
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)f, (__bf16)0.f};
+  return (uint16_t)__builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ void store_elem(char *base, int64_t idx, float v, bool f32) {
