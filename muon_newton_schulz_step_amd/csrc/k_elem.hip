@@ -18,11 +18,12 @@ namespace muon {
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
 // fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32; NaN stays NaN)
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  const bf16x2_t v = {(__bf16)f, (__bf16)0.f};
-  return (uint16_t)__builtin_bit_cast(uint32_t, v);
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)f32x2_to_bf16x2(f, 0.f); }
 
 template <bool BF16>
 __device__ __forceinline__ float load_as_f32(const void *p, int64_t i) {
@@ -130,8 +131,8 @@ __device__ __forceinline__ void load4(const void *p, int64_t i, float *v) {
 __device__ __forceinline__ void store4(void *p, int64_t i, const float *v, bool bf16) {
   if (bf16) {
     uint2 w;
-    w.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-    w.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    w.x = f32x2_to_bf16x2(v[0], v[1]);
+    w.y = f32x2_to_bf16x2(v[2], v[3]);
     *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p) + i) = w;
   } else {
     *reinterpret_cast<float4 *>(static_cast<float *>(p) + i) = make_float4(v[0], v[1], v[2], v[3]);
