@@ -100,8 +100,6 @@ def _finite_and_covered(torch, parts_flat, wl, offsets):
     # every matrix received a non-trivial update of the expected size: the
     # unscaled output has Frobenius norm sqrt(sum f^5(sigma)^2) <= 1.21 sqrt(m)
     for i, ((r, c), off) in enumerate(zip(wl.shapes, offsets)):
-        if i % 7:
-            continue
         u = parts_flat[off:off + r * c].double()
         h = wl.heads[i] or 1
         m = min(r // h, c)
@@ -150,14 +148,15 @@ def test_llama7b_full_group_sampled(torch):
 
 def test_share70b_full_group_sampled(torch):
     """The 70B single-GPU share (8 layers, 56 matrices, 6.85 G elements) in
-    the bench's launch configuration.  The oracle checks the k and v
-    projections (8192 x 1024, tall: 1024 x 8192 blocks on the large-tile
-    kernel, shape scale 2.83) of the first and last layer; the 8192-wide
-    matrices would take the fp64 oracle minutes each, so every matrix of the
-    group gets the size-independent checks instead."""
+    the bench's launch configuration.  The oracle checks the first layer's q
+    (8192 x 8192, about 20 s of fp64 oracle), the k and v projections
+    (8192 x 1024, tall: 1024 x 8192 blocks on the large-tile kernel, shape
+    scale 2.83) of the first and last layer; the 28672-wide matrices would
+    take the oracle about a minute each, so every matrix of the group gets the
+    size-independent checks instead."""
     wl = W.share70b()
     L = len(wl.shapes)
-    sample = [1, 2, L - 5]                # layer 0 k, v; layer 7 k
+    sample = [0, 1, 2, L - 5]             # layer 0 q, k, v; layer 7 k
     got, want, parts_flat, offsets, P, g = _run_group(torch, wl, "standard", sample)
     for i in sample:
         err = O.rel_frobenius(got[i], want[i])
