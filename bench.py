@@ -102,6 +102,22 @@ TRAFFIC_SOURCES = ("muon_newton_schulz_step_amd/csrc/k_gemm256.hip", "muon_newto
                    "muon_newton_schulz_step_amd/csrc/tables.hpp")
 
 
+def traffic_sources_hash() -> str:
+    """First 16 hex digits of the sha256 of the sources behind the counted
+    launches, with comments and whitespace removed (a comment edit does not
+    change the kernels the counters were taken on)."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic(workload: str):
     """HBM bytes per Newton-Schulz launch from the committed FETCH_SIZE /
     WRITE_SIZE summary, or None if it was taken on another workload or the
@@ -114,11 +130,7 @@ def measured_traffic(workload: str):
         if ":" in ln and not ln.startswith(("|", "#", "`")):
             k, _, v = ln.partition(":")
             kv[k.strip()] = v.strip()
-    h = hashlib.sha256()
-    for f in TRAFFIC_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
-    if kv.get("kernel_src_sha256_16") != h.hexdigest()[:16]:
+    if kv.get("kernel_src_sha256_16") != traffic_sources_hash():
         return None
     try:
         return float(kv["ns_gemm_traffic_bytes_per_launch"])

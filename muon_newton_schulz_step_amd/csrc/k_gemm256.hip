@@ -374,9 +374,10 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
       else fa[set][q - 4] = *reinterpret_cast<const bf16x8_t *>(la + arb[q - 4] + swz(ak[q - 4], c) * 16);
     };
     // one 16-deep k-step on fragment set `set`, in eight groups of an MFMA
-    // pair, one fragment read of the next step (RD) and one DMA instruction
-    // (DMA: instructions q0 .. q0 + 7 of stage dkt into buffer dst); the
-    // groups keep their order
+    // pair, the fragment reads of the next step (RD: two in each of the first
+    // two groups, one in each of the next four) and one DMA instruction per
+    // group (DMA: instructions q0 .. q0 + 7 of stage dkt into buffer dst);
+    // sched_barrier keeps the groups in this order
     auto kstep = [&](int set, auto rd_, int rst, int rks, auto dma_, int dkt, int dst, int q0) {
       constexpr bool RD = decltype(rd_)::value;
       constexpr bool DMA = decltype(dma_)::value;
