@@ -276,3 +276,27 @@ def test_big_tile_group(method):
     print(f"big-tile bf16 {method}: worst rel err {worst:.3e}")
     _check_padding(parts, BIG_SHAPES, offsets, P)
     _check_momentum(moms, state, res)
+
+
+BIG_HEAD_SHAPES = [(1024, 600), (768, 300), (1200, 256)]
+BIG_HEAD_COUNTS = [2, 3, 2]
+
+
+@pytest.mark.parametrize("method", ["standard", "gram"])
+def test_big_tile_head_blocks(method):
+    # head blocks on the large-tile kernel: 512 x 600 (two per matrix),
+    # 256 x 300 (three, ragged K) and 600 x 256 (two tall blocks, stored
+    # transposed), each block its own Newton-Schulz problem in the workspace
+    offsets, P = O.pack_layout(BIG_HEAD_SHAPES, 2, 16)
+    g = M.MuonGroup(BIG_HEAD_SHAPES, heads=BIG_HEAD_COUNTS, offsets=offsets, num_partitions=2, partition_numel=P,
+                    method=method, precision="bf16", grad_dtype="bf16")
+    probs = g.problems()
+    assert [(q["m"], q["n"], q["transposed"]) for q in probs] == \
+        [(512, 600, False)] * 2 + [(256, 300, False)] * 3 + [(256, 600, True)] * 2
+    micro = _micro(BIG_HEAD_SHAPES, "bf16", 0.02, 1, 1, cid=43)
+    parts, moms = run_steps(g, micro, "bf16", use_accumulate=False)
+    res, state = _oracle_run(BIG_HEAD_SHAPES, BIG_HEAD_COUNTS, offsets, 2, P, micro, "bf16", method)
+    worst = _compare(BIG_HEAD_SHAPES, offsets, parts, res, TOL["bf16"], f"big-heads/{method}")
+    print(f"big-tile head blocks bf16 {method}: worst rel err {worst:.3e}")
+    _check_padding(parts, BIG_HEAD_SHAPES, offsets, P)
+    _check_momentum(moms, state, res)
