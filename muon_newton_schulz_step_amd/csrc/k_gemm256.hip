@@ -404,21 +404,29 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 8; ++q) dma1(min(1, nkt - 1), 1, q);
+    for (int q = 0; q < 8; ++q)
+      if (nkt > 1) dma1(1, 1, q);
     read_frags(0, 0, 0);
-    // One loop body for every stage: past the end, the DMA stage index is
-    // clamped to the last stage, which reloads data into a buffer nobody
-    // reads again (the epilogue waits for those loads before reusing LDS).
-    for (int kt = 0; kt < nkt; ++kt) {
+    // One stage of the loop; DMAB / DMAA say whether stage kt+1 (B rows)
+    // and stage kt+2 (A rows) exist.  The last two stages are peeled off
+    // with those loads compiled out: a runtime test inside the MFMA groups
+    // splits them into basic blocks and costs more than it saves, and
+    // issuing them anyway (clamped to the last stage) leaves the epilogue
+    // waiting for loads nobody reads.
+    auto body = [&](int kt, auto dmab, auto dmaa) {
       const int st = kt & 1;
-      kstep(0, yes, st, 1, yes, min(kt + 1, nkt - 1), st ^ 1, 8);   // B rows of stage kt+1
+      kstep(0, yes, st, 1, dmab, kt + 1, st ^ 1, 8);   // B rows of stage kt+1
       kstep(1, yes, st, 2, no, 0, 0, 0);
       kstep(0, yes, st, 3, no, 0, 0, 0);
       // stage kt+1 landed and every wave is done reading stage kt
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      kstep(1, yes, st ^ 1, 0, yes, min(kt + 2, nkt - 1), st, 0);   // A rows of stage kt+2
-    }
+      kstep(1, yes, st ^ 1, 0, dmaa, kt + 2, st, 0);   // A rows of stage kt+2
+    };
+    int kt = 0;
+    for (; kt < nkt - 2; ++kt) body(kt, yes, yes);
+    if (kt == nkt - 2) { body(kt, yes, no); ++kt; }
+    body(kt, no, no);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   } else {
   stage(0, 0);
