@@ -29,7 +29,7 @@ the numeric definition of the step is the plain reading of that prose):
   partitions": Newton-Schulz runs on the full reduced gradient of a matrix
   that spans several partitions; each owner keeps its local slice.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 momentum is the lerp m <- beta*m + (1-beta)*G started from zero; the update
 fed to Newton-Schulz is the Nesterov blend (1-beta)*G + beta*m_new; each
 Newton-Schulz block is divided by (Frobenius norm + eps) in the wide
