@@ -164,3 +164,38 @@ def test_share70b_full_group_sampled(torch):
         assert err <= TOL_BF16
     _finite_and_covered(torch, parts_flat, wl, offsets)
     assert g.stats()["ns_invocations"] == L
+
+
+def test_llama7b_full_group_gram_sampled(torch):
+    """The Llama-7B group in the Gram form: its 4096-row blocks run the
+    split-bf16 m x m chain on the large-tile kernel.  Same sample as the
+    standard form (every matrix kind)."""
+    torch.cuda.empty_cache()
+    wl = W.llama7b()
+    sample = [0, 4, len(wl.shapes) - 1]
+    got, want, parts_flat, offsets, P, g = _run_group(torch, wl, "gram", sample)
+    for i in sample:
+        err = O.rel_frobenius(got[i], want[i])
+        print(f"llama7b group (gram), matrix {i} {wl.shapes[i]}: rel err {err:.3e}")
+        assert err <= TOL_BF16
+    _finite_and_covered(torch, parts_flat, wl, offsets)
+    assert g.stats()["ns_invocations"] == 224
+
+
+def test_share70b_full_group_gram_sampled(torch):
+    """The 70B share in the Gram form: the first layer's q (8192 x 8192, the
+    split-bf16 chain at its largest; about 25 s of fp64 oracle) and the k / v
+    projections of the first and last layer (1024 x 8192 blocks, chain of
+    1024 x 1024 products), plus the size-independent checks on every
+    matrix."""
+    torch.cuda.empty_cache()
+    wl = W.share70b()
+    L = len(wl.shapes)
+    sample = [0, 1, 2, L - 5]
+    got, want, parts_flat, offsets, P, g = _run_group(torch, wl, "gram", sample)
+    for i in sample:
+        err = O.rel_frobenius(got[i], want[i])
+        print(f"70B share (gram), matrix {i} {wl.shapes[i]}: rel err {err:.3e}")
+        assert err <= TOL_BF16
+    _finite_and_covered(torch, parts_flat, wl, offsets)
+    assert g.stats()["ns_invocations"] == L
