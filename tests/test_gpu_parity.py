@@ -174,6 +174,29 @@ def test_nesterov_off_and_beta():
     _check_momentum(moms, state, res)
 
 
+DEGEN_SHAPES = [(1, 1), (1, 2), (2, 1), (3, 3), (1, 300), (257, 1)]
+
+
+@pytest.mark.parametrize("precision", ["fp32", "bf16"])
+@pytest.mark.parametrize("method", ["standard", "gram"])
+def test_degenerate_shapes_and_beta_zero(precision, method):
+    # single elements, single rows and columns (rank-one blocks, 1 x 1
+    # Newton-Schulz problems) crossing two partitions, with beta = 0 so the
+    # momentum is the gradient itself
+    offsets, P = O.pack_layout(DEGEN_SHAPES, 2, 16)
+    g = M.MuonGroup(DEGEN_SHAPES, offsets=offsets, num_partitions=2, partition_numel=P, method=method,
+                    precision=precision, grad_dtype="fp32", beta=0.0)
+    micro = _micro(DEGEN_SHAPES, "fp32", 1.0, 1, 2, cid=51)
+    parts, moms = run_steps(g, micro, "fp32", use_accumulate=False)
+    res, state = _oracle_run(DEGEN_SHAPES, [0] * len(DEGEN_SHAPES), offsets, 2, P, micro, "fp32", method, beta=0.0)
+    _compare(DEGEN_SHAPES, offsets, parts, res, TOL[precision], f"degenerate/{method}/{precision}")
+    _check_padding(parts, DEGEN_SHAPES, offsets, P)
+    _check_momentum(moms, state, res)
+    # beta = 0: the momentum after the last step is that step's gradient
+    for i, m in enumerate(moms):
+        np.testing.assert_array_equal(m, micro[-1][0][i])
+
+
 def test_zero_gradient_zero_update():
     shapes = [(33, 65), (65, 33)]
     g = M.MuonGroup(shapes, precision="bf16", grad_dtype="fp32")
