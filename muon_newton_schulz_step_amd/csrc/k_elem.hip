@@ -88,6 +88,23 @@ __global__ __launch_bounds__(256) void k0_accumulate(const K0Mat *mats, int nmat
   const bool vec = aligned16(acc + start) && aligned16(GBF16 ? (const void *)(static_cast<const uint16_t *>(g) + start)
                                                              : (const void *)(static_cast<const float *>(g) + start));
   int64_t j = start;
+  if (vec && end - start == K0_CHUNK) {
+    // a whole chunk: two 8-element groups per lane, all loads first
+    const int64_t j0 = start + 8 * threadIdx.x, j1 = j0 + 8 * 256;
+    float v0[8], v1[8];
+    load8<GBF16>(g, j0, v0);
+    load8<GBF16>(g, j1, v1);
+    if (!first) {
+      float a0[8], a1[8];
+      load8<false>(acc, j0, a0);
+      load8<false>(acc, j1, a1);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) { v0[k] = a0[k] + v0[k]; v1[k] = a1[k] + v1[k]; }
+    }
+    store8_f32(acc + j0, v0);
+    store8_f32(acc + j1, v1);
+    return;
+  }
   if (vec) {
     for (j = start + 8 * threadIdx.x; j + 8 <= end; j += 8 * 256) {
       float v[8];
@@ -264,6 +281,26 @@ __device__ __forceinline__ float k3_body(const K3Run &R, int64_t start, int64_t 
   const bool vec = aligned16(R.dst + start) &&
                    aligned16(SBF16 ? (const void *)(static_cast<const uint16_t *>(src) + R.first + start)
                                    : (const void *)(static_cast<const float *>(src) + R.first + start));
+  if (vec && end - start == K3_CHUNK) {
+    // a whole chunk: two 8-element groups per lane, both loads first
+    const int64_t j0 = start + 8 * threadIdx.x, j1 = j0 + 8 * 256;
+    float v0[8], v1[8];
+    load8<SBF16>(src, R.first + j0, v0);
+    load8<SBF16>(src, R.first + j1, v1);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      v0[k] = v0[k] * R.scale;
+      ss = fmaf(v0[k], v0[k], ss);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      v1[k] = v1[k] * R.scale;
+      ss = fmaf(v1[k], v1[k], ss);
+    }
+    store8_f32(R.dst + j0, v0);
+    store8_f32(R.dst + j1, v1);
+    return ss;
+  }
   if (vec) {
     int64_t j;
     for (j = start + 8 * threadIdx.x; j + 8 <= end; j += 8 * 256) {
@@ -397,6 +434,19 @@ __global__ __launch_bounds__(256) void k_apply(const KARun *runs, int nrun, cons
   const float decay = 1.0f - lr * wd;
   const float step = lr * nc[1];
   auto one = [&](float p, float u) { return fmaf(-step, u, p * decay); };
+  if (aligned16(R.param + start) && aligned16(R.upd + start) && end - start == KA_CHUNK) {
+    const int64_t j0 = start + 8 * threadIdx.x, j1 = j0 + 8 * 256;
+    float p0[8], u0[8], p1[8], u1[8];
+    load8<false>(R.param, j0, p0);
+    load8<false>(R.upd, j0, u0);
+    load8<false>(R.param, j1, p1);
+    load8<false>(R.upd, j1, u1);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) { p0[k] = one(p0[k], u0[k]); p1[k] = one(p1[k], u1[k]); }
+    store8_f32(R.param + j0, p0);
+    store8_f32(R.param + j1, p1);
+    return;
+  }
   if (aligned16(R.param + start) && aligned16(R.upd + start)) {
     int64_t j;
     for (j = start + 8 * threadIdx.x; j + 8 <= end; j += 8 * 256) {
