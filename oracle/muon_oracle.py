@@ -43,9 +43,23 @@ matrices are laid out back to back in a flat index space that is cut into
 equal partitions.
 
 Parity pins: every function here is pinned by a test under tests/ that checks
-it against something other than itself (SVD closed form, scalar recurrences,
-invariances, brute-force enumeration, and the Newton-Schulz call count the
-PR 8600 page prints).  No function is parity-unpinned.
+it against something other than itself, and a planted mistake in a copy of it
+is caught (tests/test_oracle_mutations.py):
+  bf16 decoding        known bit patterns (1, -5, the smallest subnormal and
+                       normal, the largest finite, -0, +-inf)
+  rel_frobenius        hand values, including 0/0, x/0 and which argument is
+                       the reference
+  Newton-Schulz forms  SVD closed form U f^T(S) V^T, rank-one and
+                       orthonormal-row inputs, Gram = standard, invariances
+  momentum, blend      scalar closed forms under a constant gradient
+  muon_step            one step from a warm momentum rebuilt by hand (fp32
+                       momentum, Nesterov blend, normalisation, SVD closed
+                       form, shape scale), so the blend, not the momentum, is
+                       what reaches Newton-Schulz
+  layout, writeback    per-element brute force of the flat index map, padding
+                       sentinels, the Newton-Schulz call count PR 8600 prints
+  norm, clip, apply    hand values and closed forms
+No function is parity-unpinned.
 """
 
 from __future__ import annotations

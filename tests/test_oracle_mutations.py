@@ -153,3 +153,125 @@ def test_apply_pins_catch_mistakes(bad, monkeypatch):
     import test_oracle_pins as T
     with pytest.raises(AssertionError):
         T.test_apply_update_closed_forms()
+
+
+# --------------------------------------------- bf16 decoding, parity metric
+
+
+def _bf16_shift15(bits):
+    u32 = bits.astype(np.uint32) << np.uint32(15)
+    return u32.view(np.float32).astype(np.float64)
+
+
+def _bf16_as_fp16(bits):
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def _bf16_low_half(bits):
+    # value placed in the low half of the fp32 word instead of the high half
+    return np.asarray(bits, dtype=np.uint16).astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _bf16_unsigned(bits):
+    return np.abs(O.bf16_bits_to_f64(bits))
+
+
+@pytest.mark.parametrize("bad", [_bf16_shift15, _bf16_as_fp16, _bf16_low_half, _bf16_unsigned])
+def test_bf16_pin_catches_decode_mistakes(bad):
+    from oracle_pins import bf16_decode_error
+    assert bf16_decode_error(bad) > 0
+
+
+def _rel_by_got(got, want):
+    got, want = np.asarray(got, np.float64), np.asarray(want, np.float64)
+    den = np.linalg.norm(got)
+    num = np.linalg.norm(got - want)
+    if den == 0.0:
+        return 0.0 if num == 0.0 else float("inf")
+    return float(num / den)
+
+
+def _rel_max_abs(got, want):
+    got, want = np.asarray(got, np.float64), np.asarray(want, np.float64)
+    den = np.max(np.abs(want)) if want.size else 0.0
+    num = np.max(np.abs(got - want)) if want.size else 0.0
+    if den == 0.0:
+        return 0.0 if num == 0.0 else float("inf")
+    return float(num / den)
+
+
+def _rel_zero_want_is_zero(got, want):
+    want = np.asarray(want, np.float64)
+    if np.linalg.norm(want) == 0.0:
+        return 0.0
+    return _REL(got, want)
+
+
+_REL = O.rel_frobenius
+
+
+def _rel_nan_on_zero(got, want):
+    got, want = np.asarray(got, np.float64), np.asarray(want, np.float64)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        return float(np.linalg.norm(got - want) / np.linalg.norm(want))
+
+
+@pytest.mark.parametrize("bad", [_rel_by_got, _rel_max_abs, _rel_zero_want_is_zero, _rel_nan_on_zero])
+def test_metric_pin_catches_mistakes(bad, monkeypatch):
+    monkeypatch.setattr(O, "rel_frobenius", bad)
+    import test_oracle_pins as T
+    with pytest.raises(AssertionError):
+        T.test_rel_frobenius_hand_values()
+
+
+# ------------------------------------------- the step's Nesterov wiring
+
+
+def _step_feeds_momentum(grads, state, shapes, heads, offsets, num_partitions, partition_numel, opt,
+                         partitions=None, grad_scale=1.0, skip=False):
+    """muon_step with the stored momentum, not the Nesterov blend, handed to
+    Newton-Schulz."""
+    res = O.StepResult()
+    res.partitions = partitions or [np.zeros(partition_numel, dtype=np.float32) for _ in range(num_partitions)]
+    for i, (rows, cols) in enumerate(shapes):
+        g = np.asarray(grads[i], dtype=np.float64).reshape(rows, cols) * float(grad_scale)
+        m_new, _u = O.momentum_update(state.momenta[i], g, opt.beta, opt.nesterov)
+        state.momenta[i] = m_new
+        y = O.muon_matrix_update(m_new.astype(np.float64), opt.method, heads[i], opt.steps, opt.coeffs, opt.eps)
+        res.updates.append(y * O.shape_scale(rows, cols))
+    return res
+
+
+def _step_blends_old_momentum(grads, state, shapes, heads, offsets, num_partitions, partition_numel, opt,
+                              partitions=None, grad_scale=1.0, skip=False):
+    """Nesterov blend formed with the momentum before this step's update."""
+    res = O.StepResult()
+    for i, (rows, cols) in enumerate(shapes):
+        g = np.asarray(grads[i], dtype=np.float64).reshape(rows, cols)
+        m_old = state.momenta[i].astype(np.float64)
+        m_new, _ = O.momentum_update(state.momenta[i], g, opt.beta, opt.nesterov)
+        state.momenta[i] = m_new
+        u = (1.0 - opt.beta) * g + opt.beta * m_old
+        y = O.muon_matrix_update(u, opt.method, heads[i], opt.steps, opt.coeffs, opt.eps)
+        res.updates.append(y * O.shape_scale(rows, cols))
+    return res
+
+
+def _step_no_shape_scale(grads, state, shapes, heads, offsets, num_partitions, partition_numel, opt,
+                         partitions=None, grad_scale=1.0, skip=False):
+    res = O.muon_step(grads, state, shapes, heads, offsets, num_partitions, partition_numel, opt)
+    rows, cols = shapes[0]
+    res.updates = [u / O.shape_scale(rows, cols) for u in res.updates]
+    return res
+
+
+@pytest.mark.parametrize("bad", [_step_feeds_momentum, _step_blends_old_momentum])
+@pytest.mark.parametrize("method", ["standard", "gram"])
+def test_step_pin_catches_wiring_mistakes(bad, method):
+    from oracle_pins import nesterov_step_error
+    assert nesterov_step_error(bad, method, (9, 17)) > 1e-4
+
+
+def test_step_pin_catches_missing_shape_scale():
+    from oracle_pins import nesterov_step_error
+    assert nesterov_step_error(_step_no_shape_scale, "standard", (17, 13)) > 1e-4

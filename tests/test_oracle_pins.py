@@ -455,3 +455,60 @@ def test_apply_update_clipped_step_has_max_norm():
     step = [-(o.astype(np.float64)) for o in out]
     total = math.sqrt(sum(float(np.dot(s, s)) for s in step))
     assert total == pytest.approx(lr * max_norm * norm / (norm + 1e-6), rel=1e-6)
+
+
+# ------------------------------------------------------ decoding and metric
+
+
+def test_bf16_decode_known_patterns():
+    from oracle_pins import bf16_decode_error
+    assert bf16_decode_error(O.bf16_bits_to_f64) == 0
+    assert bf16_decode_error(lambda b: O.as_f64(b, "bf16")) == 0
+
+
+def test_as_f64_fp32_is_exact_widening():
+    x = np.array([1.0, -0.1, 3.4028234663852886e38, 1.401298464324817e-45, -0.0], dtype=np.float32)
+    got = O.as_f64(x, "fp32")
+    assert got.dtype == np.float64
+    # every fp32 value is an fp64 value: widening changes no bit of the value
+    np.testing.assert_array_equal(got.astype(np.float32).view(np.uint32), x.view(np.uint32))
+    assert got[1] == float(np.float32(-0.1)) and got[1] != -0.1
+    with pytest.raises(ValueError):
+        O.as_f64(x, "fp16")
+
+
+def test_rel_frobenius_hand_values():
+    # ||got - want|| / ||want||, not divided by ||got||
+    assert O.rel_frobenius([1.0, 0.0], [0.0, 2.0]) == pytest.approx(math.sqrt(5.0) / 2.0, rel=1e-15)
+    assert O.rel_frobenius([0.0, 2.0], [1.0, 0.0]) == pytest.approx(math.sqrt(5.0), rel=1e-15)
+    # a 3-4-5 difference over a norm-10 reference
+    assert O.rel_frobenius([[6.0, 8.0], [0.0, 0.0]], [[3.0, 4.0], [0.0, 0.0]]) == pytest.approx(1.0, rel=1e-15)
+    assert O.rel_frobenius([[9.0, 4.0]], [[6.0, 8.0]]) == pytest.approx(0.5, rel=1e-15)
+    # equal inputs, and the 0/0 and x/0 branches
+    assert O.rel_frobenius([1.5, -2.0], [1.5, -2.0]) == 0.0
+    assert O.rel_frobenius([0.0, 0.0], [0.0, 0.0]) == 0.0
+    assert O.rel_frobenius([0.0, 1e-30], [0.0, 0.0]) == math.inf
+    # sign and scale: -want is at distance 2, 2*want at distance 1
+    w = W.gaussian((7, 5), 3, 1.0)
+    assert O.rel_frobenius(-w, w) == pytest.approx(2.0, rel=1e-14)
+    assert O.rel_frobenius(2.0 * w, w) == pytest.approx(1.0, rel=1e-14)
+
+
+def test_gather_from_partitions_brute_force():
+    # partition r, offset o holds the value of its flat index r*P + o, so
+    # reading a matrix back must give flat_offset + j at element j
+    P, R = 13, 4
+    parts = [np.arange(r * P, (r + 1) * P, dtype=np.float32) for r in range(R)]
+    for off, (rows, cols) in ((0, (3, 4)), (5, (2, 9)), (11, (5, 7)), (38, (1, 14))):
+        got = O.gather_from_partitions(parts, off, rows, cols)
+        np.testing.assert_array_equal(got, (off + np.arange(rows * cols, dtype=np.float32)).reshape(rows, cols))
+
+
+# ------------------------------------- the whole step with a warm momentum
+
+
+@pytest.mark.parametrize("shape", [(9, 17), (17, 13), (12, 12)])
+@pytest.mark.parametrize("method", ["standard", "gram"])
+def test_step_nesterov_blend_closed_form(method, shape):
+    from oracle_pins import nesterov_step_error
+    assert nesterov_step_error(O.muon_step, method, shape) < 1e-12
