@@ -111,11 +111,19 @@ typedef struct {
   int32_t reserved;        /* must be 0                                */
 } muon_layout;
 
+/* Host-side counters.  The host never reads a device skip flag, so a step
+ * enqueued with one is counted in steps and ns_invocations whether or not
+ * the flag later discards it on the device; flagged_steps says how many of
+ * the counted steps were such conditional ones.  For a run whose flags all
+ * held 0 the counts are exact: ns_invocations = matrices x steps ([8600]
+ * "The problem" results table: once per matrix per optimizer step). */
 typedef struct {
-  uint64_t steps;          /* muon_step calls that enqueued work          */
-  uint64_t ns_invocations; /* Newton-Schulz runs: one per matrix per step */
-  uint64_t accumulations;  /* muon_accumulate calls that enqueued work    */
-  uint64_t waves;          /* workspace waves per step (>= 1)             */
+  uint64_t steps;          /* muon_step / muon_step_ex calls that enqueued */
+  uint64_t ns_invocations; /* Newton-Schulz runs enqueued: one per matrix  */
+                           /* per counted step                             */
+  uint64_t accumulations;  /* muon_accumulate calls that enqueued work     */
+  uint64_t waves;          /* workspace waves per step (>= 1)              */
+  uint64_t flagged_steps;  /* counted steps enqueued with a skip flag      */
 } muon_stats;
 
 /* A contiguous owned intersection of one matrix with one partition:
@@ -157,7 +165,13 @@ muon_status muon_default_options(muon_options *out);
 muon_status muon_plan_create(muon_plan **out, const muon_matrix *mats, int32_t n,
                              const muon_options *opt, const muon_layout *layout);
 
-/* Device workspace muon_step needs, in bytes (256-byte aligned base). */
+/* Device workspace muon_step needs, in bytes (256-byte aligned base).  The
+ * caller allocates it: the library holds no device memory of its own, in
+ * place of the gather-buffer cache ([8464] "Changes": cached gather buffers
+ * capped at 256 MB and freed on destroy).  With opt.max_inflight_bytes set
+ * it is proportional to the matrices in flight, not to the whole group
+ * ([8526] description: temporary memory proportional to the largest Muon
+ * group).  Errors: INVALID_ARG for NULL. */
 muon_status muon_plan_workspace_bytes(const muon_plan *p, size_t *bytes);
 
 /* Gradient accumulation into fp32 ([8526] description; [8600] "The change":
@@ -195,8 +209,8 @@ muon_status muon_step(muon_plan *p, const void *const *grads, float *const *mome
  *   skip_flag   DEVICE pointer to an int32, or NULL.  The kernels read it
  *               when they run: non-zero = a discarded step, and nothing
  *               outside the workspace is written (momenta and partitions
- *               keep their contents).  The host never waits for it.  The
- *               plan's counters still count the call.
+ *               keep their contents).  The host never waits for it, so the
+ *               plan's counters still count the call (see muon_stats).
  *   grad_scale  multiplies every gradient element before the momentum blend,
  *               in fp32 (1/S for gradients produced under loss scale S);
  *               1.0f gives muon_step bit for bit.  Must be finite.
@@ -238,7 +252,9 @@ muon_status muon_apply_update(muon_plan *p, float *const *params, const float *c
                               const int32_t *skip_flag, float *norm_clip_out, void *ws,
                               size_t ws_bytes, void *stream);
 
-/* The writeback alone (the same kernel muon_step ends with): for every
+/* The writeback alone (the same kernel muon_step ends with; [8526]
+ * description: only the intersection of each matrix's update with a rank's
+ * partition is copied there, the alignment padding is not): for every
  * matrix i, partitions[r][...] = fp32(updates[i][j]) * fp32(sqrt(max(1,
  * rows/cols))) on the owned intersections, one IEEE round-to-nearest
  * multiply, padding untouched.  updates[i] is the unscaled Newton-Schulz

@@ -32,8 +32,39 @@ def pack_layout(shapes, num_partitions: int, align: int = 16, interior_align: bo
     return offsets, max(per, align)
 
 
+_TORCH_DT = {"fp32": "torch.float32", "bf16": "torch.bfloat16"}
+
+
+def _check_bufs(xs, numels, dtype, what: str) -> None:
+    """Refuse tensors the library would misread: wrong count, dtype, size,
+    a non-contiguous view or a host tensor.  Integers (raw device addresses)
+    are the caller's responsibility and pass through."""
+    xs = list(xs)
+    if len(xs) != len(numels):
+        raise ValueError(f"{what}: {len(xs)} buffers, the plan has {len(numels)}")
+    for i, (x, n) in enumerate(zip(xs, numels)):
+        if x is None or isinstance(x, int) or not hasattr(x, "is_contiguous"):
+            continue
+        if dtype is not None and str(x.dtype) != _TORCH_DT[dtype]:
+            raise ValueError(f"{what}[{i}]: dtype {x.dtype}, expected {_TORCH_DT[dtype]}")
+        if not x.is_contiguous():
+            raise ValueError(f"{what}[{i}]: not contiguous (a transposed or strided view?)")
+        if int(x.numel()) != int(n):
+            raise ValueError(f"{what}[{i}]: {int(x.numel())} elements, expected {int(n)}")
+
+
+def _check_device(**lists) -> None:
+    """Every tensor among the arguments lives in device memory."""
+    for what, xs in lists.items():
+        for i, x in enumerate(xs if isinstance(xs, (list, tuple)) else [xs]):
+            if getattr(x, "is_cuda", True) is False:
+                raise ValueError(f"{what}[{i}]: a host tensor; the library needs device memory")
+
+
 class MuonGroup:
-    """A plan over one group of matrices (host memory only until used)."""
+    """A plan over one group of matrices (host memory only until used).
+    Its methods check every tensor argument against the plan before the
+    call: count, dtype, element count and contiguity."""
 
     def __init__(self, shapes, heads=None, offsets=None, num_partitions: int = 1, partition_numel=None,
                  align: int = 16, method: str = "standard", precision: str = "bf16", grad_dtype: str = "bf16",
@@ -69,26 +100,66 @@ class MuonGroup:
         self.plan = muon_plan_create(mats, o, lay)
         self.workspace_bytes = muon_plan_workspace_bytes(self.plan)
 
+    # element counts of the per-matrix and per-partition buffers
+    def _mat_numels(self):
+        return [r * c for r, c in self.shapes]
+
+    def _part_numels(self):
+        return [self.partition_numel] * self.num_partitions
+
+    def _ws(self, ws) -> int:
+        """Bytes of the workspace: a tensor's own size, or, for a raw device
+        address, the plan's requirement (the caller vouches for it)."""
+        if hasattr(ws, "numel") and hasattr(ws, "element_size"):
+            if not ws.is_contiguous():
+                raise ValueError("workspace: not contiguous")
+            return int(ws.numel()) * int(ws.element_size())
+        return self.workspace_bytes
+
+    def _flag(self, flag, what: str):
+        if flag is not None and not isinstance(flag, int):
+            if str(flag.dtype) != "torch.int32" or int(flag.numel()) < 1:
+                raise ValueError(f"{what}: needs a device int32 tensor")
+
     def step(self, grads, momenta, partitions, ws, stream=None, skip_flag=None, grad_scale: float = 1.0):
+        _check_bufs(grads, self._mat_numels(), self.grad_dtype, "grads")
+        _check_bufs(momenta, self._mat_numels(), "fp32", "momenta")
+        _check_bufs(partitions, self._part_numels(), "fp32", "partitions")
+        self._flag(skip_flag, "skip_flag")
+        _check_device(grads=grads, momenta=momenta, partitions=partitions, skip_flag=skip_flag, ws=ws)
         if skip_flag is None and grad_scale == 1.0:
-            muon_step(self.plan, grads, momenta, partitions, ws, self.workspace_bytes, stream)
+            muon_step(self.plan, grads, momenta, partitions, ws, self._ws(ws), stream)
         else:
-            muon_step_ex(self.plan, grads, momenta, partitions, skip_flag, grad_scale, ws, self.workspace_bytes,
-                         stream)
+            muon_step_ex(self.plan, grads, momenta, partitions, skip_flag, grad_scale, ws, self._ws(ws), stream)
 
     def check_finite(self, grads, dtype: str, flag, ws, stream=None):
-        muon_check_finite(self.plan, grads, dtype, flag, ws, self.workspace_bytes, stream)
+        _check_bufs(grads, self._mat_numels(), dtype, "grads")
+        self._flag(flag, "flag")
+        _check_device(grads=grads, flag=flag, ws=ws)
+        muon_check_finite(self.plan, grads, dtype, flag, ws, self._ws(ws), stream)
 
     def apply_update(self, params, partitions, lr: float, weight_decay: float, max_norm: float, ws,
                      skip_flag=None, norm_clip_out=None, stream=None):
+        _check_bufs(params, self._part_numels(), "fp32", "params")
+        _check_bufs(partitions, self._part_numels(), "fp32", "partitions")
+        self._flag(skip_flag, "skip_flag")
+        if norm_clip_out is not None and not isinstance(norm_clip_out, int):
+            _check_bufs([norm_clip_out], [2], "fp32", "norm_clip_out")
+        _check_device(params=params, partitions=partitions, skip_flag=skip_flag, norm_clip_out=norm_clip_out, ws=ws)
         muon_apply_update(self.plan, params, partitions, lr, weight_decay, max_norm, skip_flag, norm_clip_out, ws,
-                          self.workspace_bytes, stream)
+                          self._ws(ws), stream)
 
     def accumulate(self, acc, grad_mb, mb_dtype: str, first: bool, ws, stream=None):
-        muon_accumulate(self.plan, acc, grad_mb, mb_dtype, first, ws, self.workspace_bytes, stream)
+        _check_bufs(acc, self._mat_numels(), "fp32", "acc")
+        _check_bufs(grad_mb, self._mat_numels(), mb_dtype, "grad_mb")
+        _check_device(acc=acc, grad_mb=grad_mb, ws=ws)
+        muon_accumulate(self.plan, acc, grad_mb, mb_dtype, first, ws, self._ws(ws), stream)
 
     def scatter(self, updates, dtype: str, partitions, ws, stream=None):
-        muon_scatter(self.plan, updates, dtype, partitions, ws, self.workspace_bytes, stream)
+        _check_bufs(updates, self._mat_numels(), dtype, "updates")
+        _check_bufs(partitions, self._part_numels(), "fp32", "partitions")
+        _check_device(updates=updates, partitions=partitions, ws=ws)
+        muon_scatter(self.plan, updates, dtype, partitions, ws, self._ws(ws), stream)
 
     def stats(self) -> dict:
         return muon_plan_stats(self.plan)

@@ -48,7 +48,7 @@ class muon_layout(C.Structure):
 
 class muon_stats(C.Structure):
     _fields_ = [("steps", C.c_uint64), ("ns_invocations", C.c_uint64), ("accumulations", C.c_uint64),
-                ("waves", C.c_uint64)]
+                ("waves", C.c_uint64), ("flagged_steps", C.c_uint64)]
 
 
 class muon_run(C.Structure):
@@ -144,11 +144,46 @@ def _dt(x) -> int:
     return x if isinstance(x, int) else DTYPE[x]
 
 
-def _ptr_table(xs):
+# (matrices, partitions) of every live plan made by muon_plan_create, so a
+# pointer table of the wrong length is refused here instead of being read
+# past its end by the library
+_PLAN_COUNTS: dict = {}
+
+
+def _counts(plan):
+    key = plan.value if isinstance(plan, C.c_void_p) else int(plan or 0)
+    return _PLAN_COUNTS.get(key)
+
+
+def _ptr_table(xs, expect=None, what: str = "table"):
+    xs = list(xs)
+    if expect is not None and len(xs) != expect:
+        raise ValueError(f"{what}: {len(xs)} entries, the plan has {expect}")
     arr = (C.c_void_p * max(1, len(xs)))()
     for i, x in enumerate(xs):
         arr[i] = _ptr(x)
     return arr
+
+
+def _nmat(plan):
+    c = _counts(plan)
+    return None if c is None else c[0]
+
+
+def _nparts(plan):
+    c = _counts(plan)
+    return None if c is None else c[1]
+
+
+def _ws_bytes(ws, ws_bytes: int) -> int:
+    """The byte count handed to the library: the caller's figure, refused if
+    it claims more than a tensor workspace holds past its data pointer."""
+    ws_bytes = int(ws_bytes)
+    if hasattr(ws, "numel") and hasattr(ws, "element_size"):
+        have = int(ws.numel()) * int(ws.element_size())
+        if ws_bytes > have:
+            raise ValueError(f"workspace: ws_bytes {ws_bytes} exceeds the tensor's {have} bytes")
+    return ws_bytes
 
 
 def muon_default_options() -> muon_options:
@@ -165,6 +200,7 @@ def muon_plan_create(matrices, options: muon_options, layout: muon_layout) -> C.
     out = C.c_void_p()
     _check(load().muon_plan_create(C.byref(out), mats, len(matrices), C.byref(options), C.byref(layout)),
            "muon_plan_create")
+    _PLAN_COUNTS[out.value] = (len(matrices), int(layout.num_partitions))
     return out
 
 
@@ -175,44 +211,52 @@ def muon_plan_workspace_bytes(plan) -> int:
 
 
 def muon_accumulate(plan, acc, grad_mb, mb_dtype: str, first: bool, ws, ws_bytes: int, stream=None) -> None:
-    _check(load().muon_accumulate(plan, _ptr_table(acc), _ptr_table(grad_mb), _dt(mb_dtype), int(bool(first)),
-                                  _ptr(ws), int(ws_bytes), _stream(stream)), "muon_accumulate")
+    n = _nmat(plan)
+    _check(load().muon_accumulate(plan, _ptr_table(acc, n, "acc"), _ptr_table(grad_mb, n, "grad_mb"),
+                                  _dt(mb_dtype), int(bool(first)), _ptr(ws), _ws_bytes(ws, ws_bytes),
+                                  _stream(stream)), "muon_accumulate")
 
 
 def muon_step(plan, grads, momenta, partitions, ws, ws_bytes: int, stream=None) -> None:
-    _check(load().muon_step(plan, _ptr_table(grads), _ptr_table(momenta), _ptr_table(partitions), _ptr(ws),
-                            int(ws_bytes), _stream(stream)), "muon_step")
+    n, r = _nmat(plan), _nparts(plan)
+    _check(load().muon_step(plan, _ptr_table(grads, n, "grads"), _ptr_table(momenta, n, "momenta"),
+                            _ptr_table(partitions, r, "partitions"), _ptr(ws), _ws_bytes(ws, ws_bytes),
+                            _stream(stream)), "muon_step")
 
 
 def muon_step_ex(plan, grads, momenta, partitions, skip_flag, grad_scale: float, ws, ws_bytes: int,
                  stream=None) -> None:
-    _check(load().muon_step_ex(plan, _ptr_table(grads), _ptr_table(momenta), _ptr_table(partitions),
-                               _ptr(skip_flag), float(grad_scale), _ptr(ws), int(ws_bytes), _stream(stream)),
-           "muon_step_ex")
+    n, r = _nmat(plan), _nparts(plan)
+    _check(load().muon_step_ex(plan, _ptr_table(grads, n, "grads"), _ptr_table(momenta, n, "momenta"),
+                               _ptr_table(partitions, r, "partitions"), _ptr(skip_flag), float(grad_scale),
+                               _ptr(ws), _ws_bytes(ws, ws_bytes), _stream(stream)), "muon_step_ex")
 
 
 def muon_check_finite(plan, grads, dtype: str, flag, ws, ws_bytes: int, stream=None) -> None:
-    _check(load().muon_check_finite(plan, _ptr_table(grads), _dt(dtype), _ptr(flag), _ptr(ws), int(ws_bytes),
-                                    _stream(stream)), "muon_check_finite")
+    _check(load().muon_check_finite(plan, _ptr_table(grads, _nmat(plan), "grads"), _dt(dtype), _ptr(flag),
+                                    _ptr(ws), _ws_bytes(ws, ws_bytes), _stream(stream)), "muon_check_finite")
 
 
 def muon_apply_update(plan, params, partitions, lr: float, weight_decay: float, max_norm: float, skip_flag,
                       norm_clip_out, ws, ws_bytes: int, stream=None) -> None:
-    _check(load().muon_apply_update(plan, _ptr_table(params), _ptr_table(partitions), float(lr),
-                                    float(weight_decay), float(max_norm), _ptr(skip_flag), _ptr(norm_clip_out),
-                                    _ptr(ws), int(ws_bytes), _stream(stream)), "muon_apply_update")
+    r = _nparts(plan)
+    _check(load().muon_apply_update(plan, _ptr_table(params, r, "params"), _ptr_table(partitions, r, "partitions"),
+                                    float(lr), float(weight_decay), float(max_norm), _ptr(skip_flag),
+                                    _ptr(norm_clip_out), _ptr(ws), _ws_bytes(ws, ws_bytes), _stream(stream)),
+           "muon_apply_update")
 
 
 def muon_scatter(plan, updates, dtype: str, partitions, ws, ws_bytes: int, stream=None) -> None:
-    _check(load().muon_scatter(plan, _ptr_table(updates), _dt(dtype), _ptr_table(partitions), _ptr(ws),
-                               int(ws_bytes), _stream(stream)), "muon_scatter")
+    _check(load().muon_scatter(plan, _ptr_table(updates, _nmat(plan), "updates"), _dt(dtype),
+                               _ptr_table(partitions, _nparts(plan), "partitions"), _ptr(ws),
+                               _ws_bytes(ws, ws_bytes), _stream(stream)), "muon_scatter")
 
 
 def muon_plan_stats(plan) -> dict:
     s = muon_stats()
     _check(load().muon_plan_stats(plan, C.byref(s)), "muon_plan_stats")
     return {"steps": s.steps, "ns_invocations": s.ns_invocations, "accumulations": s.accumulations,
-            "waves": s.waves}
+            "waves": s.waves, "flagged_steps": s.flagged_steps}
 
 
 def muon_plan_runs(plan, matrix: int) -> list:
@@ -246,6 +290,9 @@ def muon_plan_phase_ms(plan):
 
 def muon_plan_destroy(plan) -> None:
     if plan:
+        c = _counts(plan)
+        if c is not None:
+            _PLAN_COUNTS.pop(plan.value if isinstance(plan, C.c_void_p) else int(plan), None)
         load().muon_plan_destroy(plan)
 
 

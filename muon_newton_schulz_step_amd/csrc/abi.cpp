@@ -231,6 +231,7 @@ muon_status muon_step_ex(muon_plan *p, const void *const *grads, float *const *m
   }
   p->stats.steps += 1;
   p->stats.ns_invocations += (uint64_t)nmat;
+  if (skip_flag) p->stats.flagged_steps += 1;
   p->norm_ws = ws;
   return MUON_OK;
 }

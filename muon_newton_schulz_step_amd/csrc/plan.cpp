@@ -249,6 +249,33 @@ muon_status build_plan(muon_plan *p) {
     }
   }
 
+  // Index ranges of the device tables: tile coordinates are int16, tile,
+  // K1-tile and chunk indices int32 (also the grid sizes of the launches).
+  // A group beyond them is refused here rather than wrapped on the device.
+  {
+    int64_t k1_total = 0, k3_total = 0, tiles_total = 0;
+    for (const ProblemPlan &q : p->probs) {
+      const int64_t tm = cdiv(q.m, GEMM_TILE), tn = cdiv(q.n, GEMM_TILE);
+      if (tn > INT16_MAX) {
+        set_error("matrix " + std::to_string(q.matrix) + ": a side of " + std::to_string(q.n) +
+                  " elements needs more than 32767 GEMM tiles");
+        return MUON_ERR_UNSUPPORTED;
+      }
+      const auto &M = p->mats[q.matrix];
+      k1_total += cdiv(M.hr, K1_TILE) * cdiv(M.desc.cols, K1_TILE);
+      tiles_total += tm * tn + tm * (tm + 1) / 2;
+    }
+    for (const auto &M : p->mats)
+      for (const muon_run &r : M.runs) k3_total += cdiv(r.length, std::min(K3_CHUNK, KA_CHUNK));
+    int64_t k0_total = 0;
+    for (const auto &M : p->mats) k0_total += cdiv(M.desc.rows * M.desc.cols, K0_CHUNK);
+    if (k1_total > INT32_MAX || k3_total > INT32_MAX || k0_total > INT32_MAX || tiles_total > INT32_MAX ||
+        (int64_t)p->probs.size() > INT32_MAX) {
+      set_error("group too large for the launch tables (more than 2^31-1 tiles or chunks)");
+      return MUON_ERR_UNSUPPORTED;
+    }
+  }
+
   // per-matrix and per-problem data bytes
   auto matrix_bytes = [&](const MatrixPlan &M) {
     int64_t orig = rup(M.desc.rows * M.ldc * M.elem, kAlign);

@@ -199,3 +199,64 @@ def test_step_ex_check_and_apply_validation_fails_before_device():
     with pytest.raises(M.MuonError) as ei:
         M.muon_apply_update(g.plan, [0], parts, 0.1, 0.0, 1.0, None, None, ws, ws_bytes, 0)
     assert ei.value.name == "MUON_ERR_INVALID_ARG"
+
+
+def test_plan_rejects_tile_index_overflow():
+    # GEMM tile coordinates are int16 on the device: a side needing more than
+    # 32767 tiles of 128 is refused at plan creation, one tile short is not
+    with pytest.raises(M.MuonError) as ei:
+        _group([(1 << 23, 1)], precision="fp32", grad_dtype="fp32")
+    assert ei.value.name == "MUON_ERR_UNSUPPORTED"
+    assert "32767" in M.muon_last_error()
+    g = _group([(32767 * 128, 1)], precision="fp32", grad_dtype="fp32")
+    assert g.problems()[0]["n"] == 32767 * 128
+    g.close()
+
+
+def test_binding_refuses_short_pointer_tables():
+    g = _group([(8, 8), (4, 12)], grad_dtype="fp32", precision="fp32", num_partitions=2)
+    base = 1 << 40
+    ws = base + (1 << 30)
+    grads, moms, parts = [base, base + 4096], [base + 8192, base + 12288], [base + 16384, base + 20480]
+    with pytest.raises(ValueError, match="grads"):
+        M.muon_step(g.plan, grads[:1], moms, parts, ws, g.workspace_bytes, 0)
+    with pytest.raises(ValueError, match="partitions"):
+        M.muon_step_ex(g.plan, grads, moms, parts[:1], None, 1.0, ws, g.workspace_bytes, 0)
+    with pytest.raises(ValueError, match="grad_mb"):
+        M.muon_accumulate(g.plan, moms, grads + [base], "fp32", True, ws, g.workspace_bytes, 0)
+    with pytest.raises(ValueError, match="params"):
+        M.muon_apply_update(g.plan, [base], parts, 0.1, 0.0, 1.0, None, None, ws, g.workspace_bytes, 0)
+    assert g.stats()["steps"] == 0 and g.stats()["flagged_steps"] == 0
+
+
+def test_group_checks_tensor_arguments():
+    torch = pytest.importorskip("torch")
+    shapes = [(8, 8), (4, 12)]
+    g = _group(shapes, grad_dtype="bf16", precision="bf16")
+    grads = [torch.zeros(s, dtype=torch.bfloat16) for s in shapes]
+    moms = [torch.zeros(s, dtype=torch.float32) for s in shapes]
+    parts = [torch.zeros(g.partition_numel, dtype=torch.float32)]
+    ws = torch.zeros(g.workspace_bytes, dtype=torch.uint8)
+    # wrong gradient dtype (fp32 handed to a bf16 plan)
+    with pytest.raises(ValueError, match="dtype"):
+        g.step([m.clone() for m in moms], moms, parts, ws)
+    # a transposed view
+    bad = [grads[0].t(), grads[1]]
+    with pytest.raises(ValueError, match="contiguous"):
+        g.step(bad, moms, parts, ws)
+    # wrong element count, wrong buffer count
+    with pytest.raises(ValueError, match="elements"):
+        g.step(grads, [moms[0], torch.zeros(4, 11)], parts, ws)
+    with pytest.raises(ValueError, match="buffers"):
+        g.step(grads[:1], moms[:1], parts, ws)
+    with pytest.raises(ValueError, match="partitions"):
+        g.step(grads, moms, [torch.zeros(g.partition_numel - 1)], ws)
+    # well-formed host tensors are still refused before any device call
+    with pytest.raises(ValueError, match="host tensor"):
+        g.step(grads, moms, parts, ws)
+    # a workspace tensor smaller than the byte count claimed for it
+    small = torch.zeros(16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="workspace"):
+        M.muon_step(g.plan, [1 << 40, (1 << 40) + 4096], [(1 << 40) + 8192, (1 << 40) + 12288],
+                    [(1 << 40) + 16384], small, g.workspace_bytes, 0)
+    assert g.stats()["steps"] == 0
