@@ -148,11 +148,12 @@ def cpu_baseline(wl, method: str, budget_s: float):
     import numpy as np
     import oracle.muon_oracle as O
     import workloads as W
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
     try:
         from threadpoolctl import threadpool_info
         threads = max([t.get("num_threads", 1) for t in threadpool_info() if t.get("user_api") == "blas"] or [1])
     except Exception:
-        threads = os.cpu_count() or 1
+        threads = affinity
 
     def nominal(s, h):
         h = h or 1
@@ -184,11 +185,13 @@ def cpu_baseline(wl, method: str, budget_s: float):
     done = {k for k, _ in timed}
     total_s = sum(kinds[k] * dt for k, dt in timed) + sum(kinds[k] * nominal(*k) / rate for k in kinds if k not in done)
     desc = ", ".join(f"{s[0]}x{s[1]}{'/%dh' % h if h else ''} ({dt:.2f} s)" for (s, h), dt in timed)
+    sampled = sum(kinds[k] for k in done)
     return {"value": round(total_s * 1e3, 1), "unit": "ms", "cores": int(threads), "kind": "oracle",
-            "sample": (f"one matrix of each kind through the oracle step (fp64 numpy): {desc}; the group time is "
-                       f"count x time per kind" + ("" if len(done) == len(kinds) else
-                                                     ", untimed kinds extrapolated by nominal flops")),
-            "extrapolated": len(done) != len(kinds)}
+            "sample": (f"{len(timed)} of the group's {len(wl.shapes)} matrices, one of each kind, through the "
+                       f"oracle step (fp64 numpy): {desc}; the group time is count x time per kind" +
+                       ("" if len(done) == len(kinds) else ", untimed kinds extrapolated by nominal flops")),
+            "extrapolated": sampled != len(timed) or len(done) != len(kinds),
+            "timed_s": round(spent, 2), "affinity_cores": int(affinity), "blas_threads": int(threads)}
 
 
 def main() -> int:
@@ -201,6 +204,11 @@ def main() -> int:
     ap.add_argument("--precision", default="bf16")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gram-steps", type=int, default=2,
+                    help="timed steps of a second leg in the Gram form when the workload runs both forms and the "
+                         "headline is the standard one (0: no Gram leg)")
+    ap.add_argument("--max-inflight-gb", type=float, default=0.0,
+                    help="cap the Newton-Schulz workspace at this many GB (the group then runs in waves)")
     ap.add_argument("--calibrate-copy", type=float, default=0.0,
                     help="only copy this many GiB device-to-device (a plain copy of known size, the reference "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -232,10 +240,16 @@ def main() -> int:
     method = args.method or wl.methods[0]
     offsets, P = M.pack_layout(wl.shapes, wl.num_partitions, wl.align)
     step_dtype = "fp32" if wl.gas > 1 else wl.micro_dtype
-    g = M.MuonGroup(wl.shapes, heads=wl.heads, offsets=offsets, num_partitions=wl.num_partitions,
-                    partition_numel=P, method=method, precision=args.precision, grad_dtype=step_dtype)
+    cap = int(args.max_inflight_gb * 1e9)
+
+    def make_group(meth):
+        return M.MuonGroup(wl.shapes, heads=wl.heads, offsets=offsets, num_partitions=wl.num_partitions,
+                           partition_numel=P, method=meth, precision=args.precision, grad_dtype=step_dtype,
+                           max_inflight_bytes=cap)
+
+    g = make_group(method)
     log(f"workload {wl.name}: {len(wl.shapes)} matrices, {wl.numel / 1e9:.3f} G elements, method {method}, "
-        f"precision {args.precision}, workspace {g.workspace_bytes / 1e9:.1f} GB")
+        f"precision {args.precision}, workspace {g.workspace_bytes / 1e9:.1f} GB in {g.stats()['waves']} wave(s)")
     mbs, acc, mom = make_inputs(torch, wl, 1000 * wl.config_id)
     parts_flat = torch.zeros(wl.num_partitions * P, dtype=torch.float32, device="cuda:0")
     parts = [parts_flat[r * P:(r + 1) * P] for r in range(wl.num_partitions)]
@@ -297,6 +311,45 @@ def main() -> int:
 
     probs = g.problems()
     nom, sym = ns_flops(probs, method, g.options.ns_steps)
+    waves = g.stats()["waves"]
+    ws_gb = g.workspace_bytes / 1e9
+
+    # second leg: the same group and inputs in the Gram form (the pages'
+    # default method), fewer steps; its own plan and workspace
+    gram_leg = None
+    if args.gram_steps > 0 and method != "gram" and "gram" in wl.methods:
+        g.close()
+        del ws
+        torch.cuda.empty_cache()
+        g = make_group("gram")
+        ws = torch.empty(g.workspace_bytes, dtype=torch.uint8, device="cuda:0")
+        log(f"Gram leg: workspace {g.workspace_bytes / 1e9:.1f} GB")
+        one_step()
+        torch.cuda.synchronize()
+        g.set_timing(True)
+        gp = []
+        for i in range(args.gram_steps):
+            if acc is not None:
+                for k in range(wl.gas):
+                    g.accumulate(acc[1], mbs[k % len(mbs)][1], wl.micro_dtype, k == 0, ws)
+                grads = acc[1]
+            else:
+                grads = mbs[0][1]
+            g.step(grads, mom[1], parts, ws)
+            gp.append(g.phase_ms())
+            log(f"Gram step {i + 1}/{args.gram_steps}: K1 {gp[-1][0]:.2f} ms, NS {gp[-1][1]:.2f} ms "
+                f"({gp[-1][3]} launches), K3 {gp[-1][2]:.2f} ms")
+        torch.cuda.synchronize()
+        gnom, gsym = ns_flops(g.problems(), "gram", g.options.ns_steps)
+        gk1, gns, gk3 = (statistics.mean(p[j] for p in gp) for j in range(3))
+        gram_leg = {"ns_method": "gram", "steps": args.gram_steps, "value": round(gk1 + gns + gk3, 3),
+                    "unit": "ms",
+                    "phases_ms": {"k1_norm": round(gk1, 3), "newton_schulz": round(gns, 3), "k3_scatter": round(gk3, 3)},
+                    "ns_launches": gp[-1][3],
+                    "ns_tflops_algorithmic": round(gsym / (gns * 1e-3) / 1e12, 1),
+                    "ns_frac_algorithmic": round(gsym / (gns * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                    "ns_tflops_nominal": round(gnom / (gns * 1e-3) / 1e12, 1),
+                    "workspace_gb": round(g.workspace_bytes / 1e9, 1)}
     k1_ms = statistics.mean(p[0] for p in phases)
     ns_ms = statistics.mean(p[1] for p in phases)
     k3_ms = statistics.mean(p[2] for p in phases)
@@ -326,7 +379,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": wl.name, "matrices": len(wl.shapes), "numel": numel, "gas": wl.gas,
                    "partitions": wl.num_partitions, "ns_method": method, "ns_steps": g.options.ns_steps,
-                   "ns_precision": args.precision, "grad_dtype": step_dtype},
+                   "ns_precision": args.precision, "grad_dtype": step_dtype, "workspace_gb": round(ws_gb, 1),
+                   "waves": waves},
         "phases_ms": {"k1_norm": round(k1_ms, 3), "newton_schulz": round(ns_ms, 3), "k3_scatter": round(k3_ms, 3),
                       "accumulate": round(statistics.mean(acc_ms), 3) if acc is not None else None,
                       "apply_update": round(statistics.mean(apply_ms), 3)},
@@ -344,6 +398,8 @@ def main() -> int:
                      "flops_per_step": sym, "launches_per_step": nl,
                      "avg_launch_ms": round(ns_ms / max(nl, 1), 4)},
     }
+    if gram_leg is not None:
+        line["gram_leg"] = gram_leg
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample")
         line["cpu_baseline"] = cpu_baseline(wl, method, args.cpu_budget_s)

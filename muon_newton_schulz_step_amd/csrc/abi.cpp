@@ -1,8 +1,11 @@
 // C ABI entry points that touch the device: muon_step, muon_accumulate,
-// muon_scatter, muon_plan_destroy.  All argument checks run before anything
-// is enqueued.  Launch tables are uploaded into the head of the caller's
-// workspace from pinned host staging (two slots, each guarded by an event,
-// so the host never overwrites a buffer the copy engine still reads).
+// muon_scatter, muon_check_finite, muon_apply_update, muon_plan_destroy, and
+// the pieces of a step (check, table patch, launches, counters) that every
+// entry point running a step shares.
+// All argument checks run before anything is enqueued.  Launch tables are
+// uploaded into the head of the caller's workspace from pinned host staging
+// (two slots, each guarded by an event, so the host never overwrites a
+// buffer the copy engine still reads).
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
@@ -20,11 +23,7 @@ using namespace muon;
 
 namespace {
 
-struct Range {
-  uintptr_t lo, hi;
-  const char *what;
-  int64_t index;
-};
+using Range = AddrRange;
 
 muon_status check_alias(std::vector<Range> &rs) {
   std::sort(rs.begin(), rs.end(), [](const Range &a, const Range &b) { return a.lo < b.lo; });
@@ -113,22 +112,17 @@ muon_status check_ws(const muon_plan *p, void *ws, size_t ws_bytes, size_t need)
 
 }  // namespace
 
-extern "C" {
+namespace muon {
 
-muon_status muon_step(muon_plan *p, const void *const *grads, float *const *momenta, float *const *partitions, void *ws,
-                      size_t ws_bytes, void *stream) {
-  return muon_step_ex(p, grads, momenta, partitions, nullptr, 1.0f, ws, ws_bytes, stream);
-}
-
-muon_status muon_step_ex(muon_plan *p, const void *const *grads, float *const *momenta, float *const *partitions,
-                         const int32_t *skip_flag, float grad_scale, void *ws, size_t ws_bytes, void *stream) {
+muon_status step_check(muon_plan *p, const void *const *grads, float *const *momenta, float *const *partitions,
+                       const int32_t *skip_flag, float grad_scale, void *ws, size_t ws_bytes) {
   if (!p || !grads || !momenta || !partitions) { set_error("muon_step: NULL argument"); return MUON_ERR_INVALID_ARG; }
   if (!std::isfinite(grad_scale)) { set_error("muon_step: grad_scale is not finite"); return MUON_ERR_INVALID_ARG; }
   const int32_t nmat = (int32_t)p->mats.size();
   const int32_t R = p->layout.num_partitions;
   const size_t gsz = dtype_size(p->opt.grad_dtype);
-  std::vector<Range> rs;
-  rs.reserve(2 * nmat + R + 1);
+  std::vector<AddrRange> &rs = p->ranges;  // capacity reserved at plan creation
+  rs.clear();
   for (int32_t i = 0; i < nmat; ++i) {
     if (!grads[i] || !momenta[i]) { set_error("muon_step: NULL grads/momenta entry " + std::to_string(i)); return MUON_ERR_INVALID_ARG; }
     const uintptr_t n = (uintptr_t)(p->mats[i].desc.rows * p->mats[i].desc.cols);
@@ -144,14 +138,12 @@ muon_status muon_step_ex(muon_plan *p, const void *const *grads, float *const *m
   if (st != MUON_OK) return st;
   rs.push_back({(uintptr_t)ws, (uintptr_t)ws + ws_bytes, "workspace", 0});
   if (skip_flag) rs.push_back({(uintptr_t)skip_flag, (uintptr_t)skip_flag + 4, "skip_flag", 0});
-  if ((st = check_alias(rs)) != MUON_OK) return st;
+  return check_alias(rs);
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char *h = nullptr;
-  int slot = 0;
-  if ((st = acquire_slot(p, p->host_tables.size(), &h, &slot)) != MUON_OK) return st;
+void step_patch(const muon_plan *p, char *h, const void *const *grads, float *const *momenta,
+                float *const *partitions, char *wsb) {
   std::memcpy(h, p->host_tables.data(), p->host_tables.size());
-  char *wsb = static_cast<char *>(ws);
   for (const WavePlan &W : p->waves) {
     K1Prob *k1 = reinterpret_cast<K1Prob *>(h + W.off_k1);
     for (size_t j = 0; j < W.k1.size(); ++j) {
@@ -165,9 +157,13 @@ muon_status muon_step_ex(muon_plan *p, const void *const *grads, float *const *m
       runs[j].dst = partitions[r.partition] + r.offset;
     }
   }
-  if ((st = upload(p, slot, ws, p->host_tables.size(), s)) != MUON_OK) return st;
+}
 
-  if (p->timing) {
+muon_status step_launch(muon_plan *p, const int32_t *skip_flag, float grad_scale, char *wsb, void *stream,
+                        bool timed) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  timed = timed && p->timing;
+  if (timed) {
     const size_t need = 4 * p->waves.size();
     while (p->phase_events.size() < need) {
       hipEvent_t ev;
@@ -177,7 +173,7 @@ muon_status muon_step_ex(muon_plan *p, const void *const *grads, float *const *m
     }
   }
   auto mark = [&](size_t w, int k) -> hipError_t {
-    if (!p->timing) return hipSuccess;
+    if (!timed) return hipSuccess;
     return hipEventRecord((hipEvent_t)p->phase_events[4 * w + k], s);
   };
   int32_t ns_launches = 0;
@@ -225,14 +221,42 @@ muon_status muon_step_ex(muon_plan *p, const void *const *grads, float *const *m
     if ((e = mark(wi, 3)) != hipSuccess) return hip_fail(e, "hipEventRecord (timing)");
     ++wi;
   }
-  if (p->timing) {
+  if (timed) {
     p->timed_step = true;
     p->timed_launches = ns_launches;
   }
+  return MUON_OK;
+}
+
+void step_count(muon_plan *p, const int32_t *skip_flag, const void *ws) {
   p->stats.steps += 1;
-  p->stats.ns_invocations += (uint64_t)nmat;
+  p->stats.ns_invocations += (uint64_t)p->mats.size();
   if (skip_flag) p->stats.flagged_steps += 1;
   p->norm_ws = ws;
+}
+
+}  // namespace muon
+
+extern "C" {
+
+muon_status muon_step(muon_plan *p, const void *const *grads, float *const *momenta, float *const *partitions, void *ws,
+                      size_t ws_bytes, void *stream) {
+  return muon_step_ex(p, grads, momenta, partitions, nullptr, 1.0f, ws, ws_bytes, stream);
+}
+
+muon_status muon_step_ex(muon_plan *p, const void *const *grads, float *const *momenta, float *const *partitions,
+                         const int32_t *skip_flag, float grad_scale, void *ws, size_t ws_bytes, void *stream) {
+  muon_status st = step_check(p, grads, momenta, partitions, skip_flag, grad_scale, ws, ws_bytes);
+  if (st != MUON_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char *h = nullptr;
+  int slot = 0;
+  if ((st = acquire_slot(p, p->host_tables.size(), &h, &slot)) != MUON_OK) return st;
+  char *wsb = static_cast<char *>(ws);
+  step_patch(p, h, grads, momenta, partitions, wsb);
+  if ((st = upload(p, slot, ws, p->host_tables.size(), s)) != MUON_OK) return st;
+  if ((st = step_launch(p, skip_flag, grad_scale, wsb, stream, true)) != MUON_OK) return st;
+  step_count(p, skip_flag, ws);
   return MUON_OK;
 }
 

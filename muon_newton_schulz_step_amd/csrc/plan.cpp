@@ -585,6 +585,8 @@ muon_status muon_plan_create(muon_plan **out, const muon_matrix *mats, int32_t n
   muon_status st = muon::build_plan(p);
   if (st != MUON_OK) { delete p; return st; }
   p->stats.waves = p->waves.size();
+  p->patch_host.resize(p->host_tables.size());
+  p->ranges.reserve(2 * (size_t)n + (size_t)layout->num_partitions + 4);
   *out = p;
   return MUON_OK;
 }

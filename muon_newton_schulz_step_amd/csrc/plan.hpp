@@ -59,6 +59,13 @@ struct WavePlan {
   int64_t k3_base = 0;   // index of this wave's first K3 chunk over all waves
 };
 
+// Address range of one buffer of a call, for the overlap check.
+struct AddrRange {
+  uintptr_t lo, hi;
+  const char *what;
+  int64_t index;
+};
+
 // Step of the launch schedule.
 struct Launch {
   enum Kind { GEMM_OP, GEMM_F32, COPY_SCALED } kind;
@@ -85,6 +92,11 @@ struct muon_plan {
   int64_t nparts_off = 0, nparts_n = 0, nc_off = 0, nl1_off = 0;
   const void *norm_ws = nullptr;  // workspace of the last muon_step (its partials are current)
   std::vector<char> host_tables;  // serialized tables (pointers patched per call)
+  // host buffers sized at plan creation, so a step needs no host allocation:
+  // a copy of the tables to patch per call (for uploads that do not go
+  // through the pinned staging), and the ranges of the overlap check
+  std::vector<char> patch_host;
+  std::vector<muon::AddrRange> ranges;
   // lazily created HIP resources (pinned staging, events), see abi.cpp
   void *staging[2] = {nullptr, nullptr};
   size_t staging_bytes = 0;
@@ -101,4 +113,20 @@ struct muon_plan {
 
 namespace muon {
 muon_status build_plan(muon_plan *p);
+
+// The pieces of a step, shared by the entry points that run one (abi.cpp):
+//  - step_check: every argument check; nothing is enqueued;
+//  - step_patch: the plan's tables with this call's pointers, written to h
+//    (p->host_tables.size() bytes) for a workspace at wsb;
+//  - step_launch: K1, the norm, the Newton-Schulz launches and K3 on stream
+//    s, reading the tables at the head of the workspace (timed: record the
+//    phase events if timing is enabled);
+//  - step_count: the plan's counters.
+muon_status step_check(muon_plan *p, const void *const *grads, float *const *momenta, float *const *partitions,
+                       const int32_t *skip_flag, float grad_scale, void *ws, size_t ws_bytes);
+void step_patch(const muon_plan *p, char *h, const void *const *grads, float *const *momenta,
+                float *const *partitions, char *wsb);
+muon_status step_launch(muon_plan *p, const int32_t *skip_flag, float grad_scale, char *wsb, void *stream,
+                        bool timed);
+void step_count(muon_plan *p, const int32_t *skip_flag, const void *ws);
 }

@@ -68,3 +68,39 @@ def run_steps(group, micro_grads, micro_dtype: str, momenta0=None, use_accumulat
         torch.cuda.synchronize()
     del ws_t
     return [host(p) for p in parts], [host(m) for m in moms]
+
+
+def tile_errors(got, want, tile: int = 256):
+    """Relative Frobenius error of every tile x tile block of a matrix (the
+    last row and column of blocks are the ragged edge strips), as an array
+    of shape (ceil(rows/tile), ceil(cols/tile)).  A block whose reference is
+    all zeros gets 0 if the result is too, else inf."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    r, c = want.shape
+    tr, tc = -(-r // tile), -(-c // tile)
+    pr, pc = tr * tile - r, tc * tile - c
+
+    def blocks(x):
+        x = np.pad(x, ((0, pr), (0, pc)))
+        return (x * x).reshape(tr, tile, tc, tile).sum(axis=(1, 3))
+
+    num = blocks(got - want)
+    den = blocks(want)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        err = np.sqrt(num / den)
+    err[(den == 0) & (num == 0)] = 0.0
+    err[(den == 0) & (num > 0)] = np.inf
+    return err
+
+
+def assert_tiles_within(got, want, tol: float, label: str, tile: int = 256) -> float:
+    """Every block of the matrix within the relative Frobenius tolerance;
+    returns the worst block's error."""
+    err = tile_errors(got, want, tile)
+    worst = float(err.max())
+    if worst > tol:
+        i, j = np.unravel_index(int(np.argmax(err)), err.shape)
+        raise AssertionError(f"{label}: block ({i}, {j}) of {tile}x{tile} (rows {i * tile}.., cols {j * tile}..) "
+                             f"rel err {worst:.3e} > {tol}; {int((err > tol).sum())} of {err.size} blocks over")
+    return worst

@@ -17,7 +17,7 @@ import pytest
 import muon_newton_schulz_step_amd as M
 import oracle.muon_oracle as O
 import workloads as W
-from gpu_util import SENTINEL, host, run_steps, sentinel_partitions, to_device, workspace
+from gpu_util import SENTINEL, assert_tiles_within, host, run_steps, sentinel_partitions, to_device, workspace
 
 pytestmark = pytest.mark.gpu
 
@@ -67,12 +67,16 @@ def _check_momentum(moms_gpu, state, res, ulps=3):
 
 
 def _compare(shapes, offsets, parts_gpu, res, tol, label=""):
+    """Per matrix, and per 256 x 256 block of it (the last blocks being the
+    ragged edge strips), relative Frobenius error within tol: a wrong tile or
+    edge strip of a large matrix cannot hide in the matrix-level figure."""
     worst = 0.0
     for i, (r, c) in enumerate(shapes):
         got = O.gather_from_partitions(parts_gpu, offsets[i], r, c)
         err = O.rel_frobenius(got, res.updates[i])
         worst = max(worst, err)
         assert err <= tol, f"{label} matrix {i} {r}x{c}: rel err {err:.3e} > {tol}"
+        assert_tiles_within(got, res.updates[i], tol, f"{label} matrix {i} {r}x{c}")
     return worst
 
 

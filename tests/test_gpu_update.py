@@ -264,3 +264,106 @@ def test_apply_update_after_multi_wave_step(torch):
     np.testing.assert_allclose(outs[1][2], outs[0][2], rtol=1e-6)
     for a, b in zip(outs[0][1], outs[1][1]):
         np.testing.assert_allclose(b, a, rtol=1e-6, atol=1e-9)
+
+
+@pytest.mark.parametrize("precision", ["fp32", "bf16"])
+def test_training_trajectory_vs_oracle(torch, precision):
+    """Three optimizer steps run as a mixed-precision training loop runs them,
+    against the oracle's muon_step / apply_update sequence on the same bits.
+    Gradients are made under loss scale S = 2^12 and handed in with
+    grad_scale 1/S; before every step the overflow check writes the device
+    skip flag that the step and the parameter update both read; the middle
+    step's gradients hold an Inf, so that step is discarded on both sides;
+    every step ends with the clipped parameter update.
+
+    Checked after every step: the flag against the oracle's own finiteness
+    decision; momenta within 3 fp32 spacings of |beta m| + |(1-beta) g|;
+    every matrix and 256 x 256 block of the update within the Newton-Schulz
+    tolerance; the norm within that tolerance; the parameters against the
+    oracle's update of the GPU's own inputs (2 fp32 spacings).  At the end the
+    parameters against the all-oracle trajectory, within the bound the
+    update tolerance implies: sum over kept steps of lr clip ||u|| (2 tol)
+    (a relative error tol in u and at most tol in the clip factor), plus 2
+    fp32 spacings of |p| per step."""
+    from gpu_util import assert_tiles_within
+    tol = {"fp32": 1e-4, "bf16": 2e-2}[precision]
+    shapes, R = SHAPES, 3
+    g, offsets, P = _group(shapes, R, precision=precision, grad_dtype="fp32")
+    ws_t, ws = workspace(g.workspace_bytes)
+    S = 2.0 ** 12
+    lr, wd, max_norm = 0.02, 0.1, 0.5
+    beta = float(np.float32(0.95))
+    host_grads = []
+    for k in range(3):
+        gk = [W.gaussian(s, 5000 + 100 * k + i, 0.02) * np.float32(S) for i, s in enumerate(shapes)]
+        if k == 1:
+            gk[2][7, 11] = np.float32(np.inf)
+        host_grads.append(gk)
+    p0 = [W.gaussian((P,), 6000 + r, 0.5) for r in range(R)]
+
+    # HIP path
+    moms = [torch.zeros(s, dtype=torch.float32, device="cuda:0") for s in shapes]
+    parts = [torch.zeros(P, dtype=torch.float32, device="cuda:0") for _ in range(R)]
+    params = [to_device(p, "fp32") for p in p0]
+    flag = _flag(torch, 0)
+    nc = torch.zeros(2, dtype=torch.float32, device="cuda:0")
+
+    # oracle
+    opt = O.MuonOptions(beta=beta, method="standard", eps=float(np.float32(O.NORM_EPS)))
+    state = O.init_state(shapes)
+    parts_o = [np.zeros(P, dtype=np.float32) for _ in range(R)]
+    params_o = [p.copy() for p in p0]
+    bound_u = 0.0
+    for k in range(3):
+        dev = [to_device(x, "fp32") for x in host_grads[k]]
+        g.check_finite(dev, "fp32", flag, ws)
+        before = [host(p).copy() for p in params]
+        g.step(dev, moms, parts, ws, skip_flag=flag, grad_scale=1.0 / S)
+        g.apply_update(params, parts, lr, wd, max_norm, ws, skip_flag=flag, norm_clip_out=nc)
+        torch.cuda.synchronize()
+
+        skip = not all(np.all(np.isfinite(x)) for x in host_grads[k])
+        assert int(flag.item()) == int(skip), f"step {k}: overflow flag"
+        grads64 = [O.as_f64(x, "fp32") for x in host_grads[k]]
+        scale_terms = None if skip else [np.abs(beta * m.astype(np.float64)) + np.abs((1 - beta) * gg / S)
+                                         for m, gg in zip(state.momenta, grads64)]
+        O.muon_step(grads64, state, shapes, [0] * len(shapes), offsets, R, P, opt, partitions=parts_o,
+                    grad_scale=1.0 / S, skip=skip)
+        params_o, norm_o, clip_o = O.apply_update(params_o, parts_o, shapes, offsets, lr, wd, max_norm, skip=skip)
+
+        for i, (got, want) in enumerate(zip([host(m) for m in moms], state.momenta)):
+            if skip:
+                continue
+            bound = 3 * np.spacing(scale_terms[i].astype(np.float32)).astype(np.float64)
+            diff = np.abs(got.astype(np.float64) - want.astype(np.float64))
+            assert np.all(diff <= bound), f"step {k} momentum {i}"
+        hp = [host(p) for p in parts]
+        for i, (r, c) in enumerate(shapes):
+            got_u = O.gather_from_partitions(hp, offsets[i], r, c)
+            want_u = O.gather_from_partitions(parts_o, offsets[i], r, c)
+            err = O.rel_frobenius(got_u, want_u)
+            assert err <= tol, f"step {k} matrix {i}: update rel err {err:.3e}"
+            assert_tiles_within(got_u, want_u, tol, f"step {k} matrix {i}")
+        got_p = [host(p) for p in params]
+        if skip:
+            for a, b in zip(got_p, before):
+                np.testing.assert_array_equal(a, b)
+            continue
+        got_norm, got_clip = (float(v) for v in host(nc))
+        assert got_norm == pytest.approx(norm_o, rel=tol)
+        assert got_clip == pytest.approx(clip_o, rel=2 * tol)
+        assert clip_o < 1.0, "max_norm is meant to clip"
+        want_p, _, clip_g = O.apply_update(before, hp, shapes, offsets, lr, wd, max_norm)
+        _check_params(got_p, want_p, before, hp, lr, wd, clip_g)
+        bound_u += lr * clip_o * norm_o * 2 * tol
+
+    st = g.stats()
+    n = len(shapes)
+    assert st["steps"] == 3 and st["ns_invocations"] == 3 * n and st["flagged_steps"] == 3
+    assert state.steps == 2 and state.ns_invocations == 2 * n
+    got_p = np.concatenate([host(p) for p in params]).astype(np.float64)
+    want_p = np.concatenate(params_o).astype(np.float64)
+    spacing = np.linalg.norm(2 * np.spacing(np.abs(want_p).astype(np.float32)).astype(np.float64)) * 2
+    dev_p = float(np.linalg.norm(got_p - want_p))
+    print(f"{precision}: parameter deviation {dev_p:.3e} against bound {bound_u + spacing:.3e}")
+    assert dev_p <= bound_u + spacing
