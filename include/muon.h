@@ -222,6 +222,31 @@ muon_status muon_step_ex(muon_plan *p, const void *const *grads, float *const *m
                          float *const *partitions, const int32_t *skip_flag, float grad_scale,
                          void *ws, size_t ws_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (a serving loop that may
+ * not call hipMalloc, a harness that forbids allocation, code that wants no
+ * caller workspace at all): muon_step_ex with the same kernels, arguments
+ * and results, minus the workspace.  Its workspace is a device array of
+ * MUON_NOALLOC_SCRATCH_BYTES compiled into the library; each GPU the library
+ * runs on holds one copy from the first call on it until the process ends.
+ * The launch tables reach that array as kernel arguments (at most 96 KB of
+ * tables, copied by the runtime at launch), so the call allocates nothing:
+ * no hipMalloc, hipHostMalloc or hipFree, and no host heap on success.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents; the step writes every byte it later reads, so nothing
+ *     needs clearing between calls.  Calls that can overlap on one GPU (two
+ *     streams, two host threads) race on it: the caller orders them.
+ *   - The update-norm partials it leaves stay in the array, so
+ *     muon_apply_update cannot follow it (it reports that no step ran on its
+ *     workspace); run muon_step_ex when the parameter update follows.
+ * Errors: WORKSPACE if the plan's workspace (muon_plan_workspace_bytes)
+ * exceeds MUON_NOALLOC_SCRATCH_BYTES (max_inflight_bytes can cut it into
+ * waves that fit); UNSUPPORTED if its tables exceed 96 KB; then as
+ * muon_step_ex. */
+#define MUON_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+muon_status muon_step_noalloc(muon_plan *p, const void *const *grads, float *const *momenta,
+                              float *const *partitions, const int32_t *skip_flag, float grad_scale,
+                              void *stream);
+
 /* Overflow check on the step's gradients: *flag (DEVICE int32) = 1 if any
  * element of any grads[i] (rows x cols, `dtype`) is Inf or NaN, else 0.
  * The result can be handed to muon_step_ex / muon_apply_update as their

@@ -13,7 +13,7 @@ from ._lib import (DTYPE, EXPORTS, NS_METHOD, PRECISION, MuonError, load, muon_a
                    muon_apply_update, muon_check_finite, muon_default_options, muon_last_error, muon_layout,
                    muon_plan_create, muon_plan_destroy, muon_plan_phase_ms, muon_plan_problems, muon_plan_runs,
                    muon_plan_set_timing, muon_plan_stats, muon_plan_workspace_bytes, muon_scatter,
-                   muon_status_string, muon_step, muon_step_ex)
+                   muon_status_string, muon_step, muon_step_ex, muon_step_noalloc)
 
 __all__ = ["MuonGroup", "pack_layout", "MuonError", "load"] + list(EXPORTS)
 
@@ -131,6 +131,15 @@ class MuonGroup:
             muon_step(self.plan, grads, momenta, partitions, ws, self._ws(ws), stream)
         else:
             muon_step_ex(self.plan, grads, momenta, partitions, skip_flag, grad_scale, ws, self._ws(ws), stream)
+
+    def step_noalloc(self, grads, momenta, partitions, stream=None, skip_flag=None, grad_scale: float = 1.0):
+        """The step on the library's static workspace (no caller workspace)."""
+        _check_bufs(grads, self._mat_numels(), self.grad_dtype, "grads")
+        _check_bufs(momenta, self._mat_numels(), "fp32", "momenta")
+        _check_bufs(partitions, self._part_numels(), "fp32", "partitions")
+        self._flag(skip_flag, "skip_flag")
+        _check_device(grads=grads, momenta=momenta, partitions=partitions, skip_flag=skip_flag)
+        muon_step_noalloc(self.plan, grads, momenta, partitions, skip_flag, grad_scale, stream)
 
     def check_finite(self, grads, dtype: str, flag, ws, stream=None):
         _check_bufs(grads, self._mat_numels(), dtype, "grads")

@@ -26,7 +26,7 @@ DTYPE = {"fp32": 0, "bf16": 1}
 
 # every symbol include/muon.h declares
 EXPORTS = ("muon_default_options", "muon_plan_create", "muon_plan_workspace_bytes", "muon_accumulate",
-           "muon_step", "muon_step_ex", "muon_check_finite", "muon_apply_update", "muon_scatter",
+           "muon_step", "muon_step_ex", "muon_step_noalloc", "muon_check_finite", "muon_apply_update", "muon_scatter",
            "muon_plan_stats", "muon_plan_runs", "muon_plan_problems", "muon_plan_set_timing",
            "muon_plan_phase_ms", "muon_plan_destroy", "muon_status_string", "muon_last_error")
 
@@ -83,6 +83,7 @@ def load(path: str | None = None) -> C.CDLL:
         "muon_accumulate": (i32, [vp, C.POINTER(vp), C.POINTER(vp), i32, i32, vp, sz, vp]),
         "muon_step": (i32, [vp, C.POINTER(vp), C.POINTER(vp), C.POINTER(vp), vp, sz, vp]),
         "muon_step_ex": (i32, [vp, C.POINTER(vp), C.POINTER(vp), C.POINTER(vp), vp, C.c_float, vp, sz, vp]),
+        "muon_step_noalloc": (i32, [vp, C.POINTER(vp), C.POINTER(vp), C.POINTER(vp), vp, C.c_float, vp]),
         "muon_check_finite": (i32, [vp, C.POINTER(vp), i32, vp, vp, sz, vp]),
         "muon_apply_update": (i32, [vp, C.POINTER(vp), C.POINTER(vp), C.c_float, C.c_float, C.c_float, vp, vp,
                                     vp, sz, vp]),
@@ -230,6 +231,18 @@ def muon_step_ex(plan, grads, momenta, partitions, skip_flag, grad_scale: float,
     _check(load().muon_step_ex(plan, _ptr_table(grads, n, "grads"), _ptr_table(momenta, n, "momenta"),
                                _ptr_table(partitions, r, "partitions"), _ptr(skip_flag), float(grad_scale),
                                _ptr(ws), _ws_bytes(ws, ws_bytes), _stream(stream)), "muon_step_ex")
+
+
+# size of the library's static workspace array (MUON_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def muon_step_noalloc(plan, grads, momenta, partitions, skip_flag=None, grad_scale: float = 1.0,
+                      stream=None) -> None:
+    n, r = _nmat(plan), _nparts(plan)
+    _check(load().muon_step_noalloc(plan, _ptr_table(grads, n, "grads"), _ptr_table(momenta, n, "momenta"),
+                                    _ptr_table(partitions, r, "partitions"), _ptr(skip_flag), float(grad_scale),
+                                    _stream(stream)), "muon_step_noalloc")
 
 
 def muon_check_finite(plan, grads, dtype: str, flag, ws, ws_bytes: int, stream=None) -> None:

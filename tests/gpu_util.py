@@ -71,10 +71,18 @@ def run_steps(group, micro_grads, micro_dtype: str, momenta0=None, use_accumulat
 
 
 def tile_errors(got, want, tile: int = 256):
-    """Relative Frobenius error of every tile x tile block of a matrix (the
-    last row and column of blocks are the ragged edge strips), as an array
-    of shape (ceil(rows/tile), ceil(cols/tile)).  A block whose reference is
-    all zeros gets 0 if the result is too, else inf."""
+    """Error of every tile x tile block of a matrix (the last row and column
+    of blocks are the ragged edge strips), as (err, allowed) arrays of shape
+    (ceil(rows/tile), ceil(cols/tile)).
+
+    err is the block's error norm over the norm a block of its size has at
+    the matrix's RMS magnitude, ||d_block|| / (rms(want) sqrt(N_block)): for a
+    block of typical magnitude it is the block's relative Frobenius error.
+    allowed(tol) = tol (1 + 3 / sqrt(N_block)): a block's error ratio
+    fluctuates around the matrix-level one by about 1/sqrt(N_block) of it, so
+    a whole 256 x 256 block gets tol within 1.2% while a one-element corner
+    block gets 4 tol; a wrong tile or strip (errors the size of the values
+    themselves) exceeds either by orders of magnitude."""
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)
     r, c = want.shape
@@ -86,21 +94,24 @@ def tile_errors(got, want, tile: int = 256):
         return (x * x).reshape(tr, tile, tc, tile).sum(axis=(1, 3))
 
     num = blocks(got - want)
-    den = blocks(want)
+    cnt = blocks(np.ones_like(want))
+    rms2 = float(np.sum(want * want)) / want.size
     with np.errstate(divide="ignore", invalid="ignore"):
-        err = np.sqrt(num / den)
-    err[(den == 0) & (num == 0)] = 0.0
-    err[(den == 0) & (num > 0)] = np.inf
-    return err
+        err = np.sqrt(num / (rms2 * cnt))
+    if rms2 == 0.0:
+        err = np.where(num == 0, 0.0, np.inf)
+    slack = 1.0 + 3.0 / np.sqrt(cnt)
+    return err, slack
 
 
 def assert_tiles_within(got, want, tol: float, label: str, tile: int = 256) -> float:
-    """Every block of the matrix within the relative Frobenius tolerance;
-    returns the worst block's error."""
-    err = tile_errors(got, want, tile)
-    worst = float(err.max())
-    if worst > tol:
-        i, j = np.unravel_index(int(np.argmax(err)), err.shape)
+    """Every block of the matrix within tol (1 + 3/sqrt(N_block)) by the
+    measure of tile_errors; returns the worst block's error ratio."""
+    err, slack = tile_errors(got, want, tile)
+    over = err > tol * slack
+    if over.any():
+        i, j = np.unravel_index(int(np.argmax(err / slack)), err.shape)
         raise AssertionError(f"{label}: block ({i}, {j}) of {tile}x{tile} (rows {i * tile}.., cols {j * tile}..) "
-                             f"rel err {worst:.3e} > {tol}; {int((err > tol).sum())} of {err.size} blocks over")
-    return worst
+                             f"error {err[i, j]:.3e} > {tol * slack[i, j]:.3e}; {int(over.sum())} of {err.size} "
+                             f"blocks over")
+    return float(err.max())

@@ -260,3 +260,17 @@ def test_group_checks_tensor_arguments():
         M.muon_step(g.plan, [1 << 40, (1 << 40) + 4096], [(1 << 40) + 8192, (1 << 40) + 12288],
                     [(1 << 40) + 16384], small, g.workspace_bytes, 0)
     assert g.stats()["steps"] == 0
+
+
+def test_noalloc_scratch_size_matches_header_and_refuses_large_plans():
+    text = open(os.path.join(ROOT, "include", "muon.h")).read()
+    m = re.search(r"#define MUON_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.NOALLOC_SCRATCH_BYTES
+    g = _group([(4096, 4096)])
+    assert g.workspace_bytes > _lib.NOALLOC_SCRATCH_BYTES
+    base = 1 << 40
+    with pytest.raises(M.MuonError) as ei:
+        M.muon_step_noalloc(g.plan, [base], [base + (1 << 26)], [base + (1 << 28)], None, 1.0, 0)
+    assert ei.value.name == "MUON_ERR_WORKSPACE"
+    assert "max_inflight_bytes" in M.muon_last_error()
+    assert g.stats()["steps"] == 0
