@@ -74,7 +74,8 @@ typedef enum { MUON_NS_STANDARD = 0, MUON_NS_GRAM = 1 } muon_ns_method;
 /* Arithmetic of Newton-Schulz.  FP32: fp32 operands and accumulation
  * throughout.  BF16: bf16 MFMA operands with fp32 accumulation; the Gram
  * form's small-side chain (R, P, Q) is fp32 for blocks with m < 256 and a
- * split-bf16 pair (hi + lo, three bf16 products per product) for m >= 256. */
+ * split-bf16 pair (hi + lo, three bf16 products per product) for m >= 256,
+ * except that blocks with m >= 2048 accumulate Q with one bf16 product. */
 typedef enum { MUON_PREC_FP32 = 0, MUON_PREC_BF16 = 1 } muon_ns_precision;
 
 /* Storage type of a gradient or update buffer. */

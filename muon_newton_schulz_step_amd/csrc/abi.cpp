@@ -200,11 +200,11 @@ muon_status step_launch(muon_plan *p, const int32_t *skip_flag, float grad_scale
     } else {
       // large bf16 problems first (the bulk of the work), then small bf16
       // ones, then fp32-operand ones
-      for (int grp = PG_BF16_BIG; grp >= PG_F32; --grp) {
+      for (int grp = NGROUPS - 1; grp >= PG_F32; --grp) {
         if (W.tiles[grp][TL_MN128].empty()) continue;
-        const std::vector<Launch> &sched = p->schedule[grp == PG_F32 ? 0 : (grp == PG_BF16 ? 1 : 2)];
+        const std::vector<Launch> &sched = p->schedule[grp];
         for (const Launch &L : sched) {
-          const bool big = grp == PG_BF16_BIG && L.kind == Launch::GEMM_OP;
+          const bool big = grp >= PG_BF16_BIG && L.kind == Launch::GEMM_OP;
           const int list = big ? (L.mn ? TL_MN256 : TL_MM256) : (L.mn ? TL_MN128 : TL_MM128);
           const TileDev *tl = reinterpret_cast<const TileDev *>(wsb + W.off_tiles[grp][list]);
           const int nt = (int)W.tiles[grp][list].size();

@@ -233,6 +233,8 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
   int64_t dA1 = 0, dA2 = 0, dB1 = 0, dB2 = 0;
   if (SPLIT && R.nseg > 1) {
     dA1 = P.off[R.rA2[0]] - P.off[R.rA]; dB1 = P.off[R.rB2[0]] - P.off[R.rB];
+  }
+  if (SPLIT && R.nseg > 2) {
     dA2 = P.off[R.rA2[1]] - P.off[R.rA]; dB2 = P.off[R.rB2[1]] - P.off[R.rB];
   }
   const int64_t m0 = (int64_t)tile.tm * BT, n0 = (int64_t)tile.tn * BT;

@@ -61,7 +61,7 @@ static std::vector<muon_run> make_runs(int32_t mi, int64_t off, int64_t numel, i
 // matrix is a pair hi = bf16(v), lo = bf16(v - hi), and every chain product
 // X Y^T is hi_X hi_Y^T + hi_X lo_Y^T + lo_X hi_Y^T (three K segments of the
 // bf16 kernel, fp32 accumulation), about 16 significant bits per entry.
-static std::vector<Launch> build_split_gram_schedule(const muon_options &o) {
+static std::vector<Launch> build_split_gram_schedule(const muon_options &o, bool lean_q) {
   const int T = o.ns_steps;
   std::vector<Launch> S;
   auto base = [&](int rS0, int rS1, int flags, float cd, float cacc, float cdiag) {
@@ -111,7 +111,15 @@ static std::vector<Launch> build_split_gram_schedule(const muon_options &o) {
     if (k == 1) qcur = R_Q0;
     else {
       const int qn = (qcur == R_Q0) ? R_Q1 : R_Q0;
-      S.push_back(Launch{Launch::GEMM_OP, split(base(qn, lo_of(qn), SP, 0.f, 1.f, 0.f), Pr, qcur), false});
+      if (lean_q) {
+        // Q <- P Q from the high halves, stored as bf16 only: Q reaches the
+        // output through its bf16 value anyway (Y = s Q_hi X0)
+        GemmRecipe rq = base(qn, -1, GF_SYM, 0.f, 1.f, 0.f);
+        rq.rA = (int8_t)Pr; rq.rB = (int8_t)qcur;
+        S.push_back(Launch{Launch::GEMM_OP, rq, false});
+      } else {
+        S.push_back(Launch{Launch::GEMM_OP, split(base(qn, lo_of(qn), SP, 0.f, 1.f, 0.f), Pr, qcur), false});
+      }
       qcur = qn;
     }
     if (!last) {
@@ -312,9 +320,10 @@ muon_status build_plan(muon_plan *p) {
     p->waves.push_back(std::move(cur));
   }
 
-  p->schedule[0] = build_schedule(o, false);
-  p->schedule[1] = build_schedule(o, true);
-  p->schedule[2] = standard ? p->schedule[1] : build_split_gram_schedule(o);
+  p->schedule[PG_F32] = build_schedule(o, false);
+  p->schedule[PG_BF16] = build_schedule(o, true);
+  p->schedule[PG_BF16_BIG] = standard ? p->schedule[PG_BF16] : build_split_gram_schedule(o, false);
+  p->schedule[PG_BF16_LEAN] = standard ? p->schedule[PG_BF16] : build_split_gram_schedule(o, true);
 
   int64_t max_k1 = 0, max_probs = 0, max_data = 0, nparts = 0;
   for (size_t w = 0; w < p->waves.size(); ++w) {
@@ -417,7 +426,9 @@ muon_status build_plan(muon_plan *p) {
       W.k1.push_back(k);
       W.k1_matrix.push_back(q.matrix);
 
-      const int grp = M.ops32 ? PG_F32 : (q.m >= BIG_TILE_MIN_M ? PG_BF16_BIG : PG_BF16);
+      const int grp = M.ops32 ? PG_F32
+                      : q.m < BIG_TILE_MIN_M ? PG_BF16
+                      : (!standard && q.m >= GRAM_LEAN_MIN_M) ? PG_BF16_LEAN : PG_BF16_BIG;
       // Tiles of a problem in 4 x 8 blocks (block-row-major, row-major inside
       // a block): the large-tile kernel hands each XCD 32 consecutive
       // entries, i.e. one block, whose 12 operand panels its L2 then shares.
@@ -436,7 +447,7 @@ muon_status build_plan(muon_plan *p) {
                 W.tiles[grp][lmn].push_back(TileDev{(int32_t)li, (int16_t)a, (int16_t)b});
       };
       add_tiles(GEMM_TILE, TL_MM128, TL_MN128);
-      if (grp == PG_BF16_BIG) add_tiles(BIG_TILE, TL_MM256, TL_MN256);
+      if (grp >= PG_BF16_BIG) add_tiles(BIG_TILE, TL_MM256, TL_MN256);
     }
     W.k1_tiles = k1t;
     max_k1 = std::max<int64_t>(max_k1, k1t);

@@ -81,9 +81,11 @@ struct muon_plan {
   std::vector<muon::MatrixPlan> mats;
   std::vector<muon::ProblemPlan> probs;
   std::vector<muon::WavePlan> waves;
-  // launch schedules: [0] fp32 operands, [1] bf16 operands, [2] bf16 large
-  // blocks (the split-bf16 Gram chain; equal to [1] for the standard form)
-  std::vector<muon::Launch> schedule[3];
+  // launch schedule per problem group: [PG_F32] fp32 operands, [PG_BF16]
+  // bf16 operands, [PG_BF16_BIG] bf16 large blocks (the split-bf16 Gram
+  // chain; equal to [PG_BF16] for the standard form), [PG_BF16_LEAN] the
+  // Gram chain with a one-product Q accumulation
+  std::vector<muon::Launch> schedule[muon::NGROUPS];
   int64_t tables_bytes = 0;  // all waves' tables, at the head of the workspace
   int64_t partials_off = 0, scales_off = 0, data_off = 0, ws_bytes = 0;
   int64_t max_k1_tiles = 0, max_probs = 0;

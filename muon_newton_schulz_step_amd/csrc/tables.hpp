@@ -38,8 +38,17 @@ constexpr int BIG_TILE = 256;
 constexpr int BIG_TILE_MIN_M = MUON_BIG_TILE_MIN_M;
 
 // Problem groups of a wave: fp32 operands; bf16 with m < BIG_TILE; bf16 with
-// m >= BIG_TILE.  Tile lists per group: m x m and m x n, at each tile size.
-enum ProbGroup : int { PG_F32 = 0, PG_BF16 = 1, PG_BF16_BIG = 2, NGROUPS };
+// m >= BIG_TILE; and, in the Gram form only, bf16 blocks with
+// m >= GRAM_LEAN_MIN_M, whose chain accumulates Q with one bf16 product
+// (below).  Tile lists per group: m x m and m x n, at each tile size.
+enum ProbGroup : int { PG_F32 = 0, PG_BF16 = 1, PG_BF16_BIG = 2, PG_BF16_LEAN = 3, NGROUPS };
+
+// Gram form, bf16 blocks with m >= this: Q <- P Q is one bf16 product of
+// the high halves, stored as bf16 (three-segment split products for the
+// R chain and the square of R, as for smaller blocks).  Emulated error on
+// Gaussian inputs: 1.2e-2 at 2048 x 2048, 1.4e-2 at 1024 x 1024 (the full
+// split chain: 6.9e-3, 8.8e-3), falling with the block size.
+constexpr int GRAM_LEAN_MIN_M = 2048;
 enum TileList : int { TL_MM128 = 0, TL_MN128, TL_MM256, TL_MN256, NLISTS };
 
 // Newton-Schulz blocks whose small side is below this run on fp32 operands

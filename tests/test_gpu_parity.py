@@ -305,6 +305,25 @@ def test_big_tile_group(method):
     _check_momentum(moms, state, res)
 
 
+LEAN_SHAPES = [(2048, 2048), (2304, 2112), (3000, 2080), (1024, 1100)]
+
+
+def test_gram_lean_q_chain():
+    # Gram blocks with m >= 2048 accumulate Q with one bf16 product: a square
+    # block, a wide and a tall one ragged against the 256 tiles (m = 2112,
+    # 2080), beside a 1024-row block on the full split chain
+    offsets, P = O.pack_layout(LEAN_SHAPES, 2, 16)
+    g = M.MuonGroup(LEAN_SHAPES, offsets=offsets, num_partitions=2, partition_numel=P, method="gram",
+                    precision="bf16", grad_dtype="bf16")
+    assert [q["m"] for q in g.problems()] == [2048, 2112, 2080, 1024]
+    micro = _micro(LEAN_SHAPES, "bf16", 0.02, 1, 1, cid=45)
+    parts, moms = run_steps(g, micro, "bf16", use_accumulate=False)
+    res, state = _oracle_run(LEAN_SHAPES, [0] * len(LEAN_SHAPES), offsets, 2, P, micro, "bf16", "gram")
+    worst = _compare(LEAN_SHAPES, offsets, parts, res, TOL["bf16"], "gram-lean")
+    print(f"gram lean Q chain: worst rel err {worst:.3e}")
+    _check_padding(parts, LEAN_SHAPES, offsets, P)
+
+
 BIG_HEAD_SHAPES = [(1024, 600), (768, 300), (1200, 256)]
 BIG_HEAD_COUNTS = [2, 3, 2]
 
