@@ -201,6 +201,13 @@ __device__ __forceinline__ uint4 mask_tail_bf16(uint4 v, int valid) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// Source of one stage of the concatenated K range: the operand bases of its
+// segment and the K offset inside that segment.
+struct Src {
+  const char *a, *b;
+  int64_t k0;
+};
+
 // SPLIT: the recipe may carry K segments, a split D and a split output; the
 // plain instance keeps the single-segment pipeline free of them.
 template <bool SPLIT>
@@ -351,19 +358,30 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
     // drains it.  The destination rows of this wave are uniform, so M0 is
     // computed on the scalar unit.
     const int wv = __builtin_amdgcn_readfirstlane(wave);
-    auto dma1 = [&](int kt, int st, int q) {
-      const int seg = !SPLIT ? 0 : (kt >= nk ? (kt >= 2 * nk ? 2 : 1) : 0);
-      const int64_t k0 = (int64_t)(kt - seg * nk) * KS;
+    // Source of stage kt of the concatenated K range: the segment's operand
+    // bases and the K offset inside the segment.  Chosen once per stage with
+    // selects, outside the MFMA groups: chosen per DMA instruction, the
+    // choice compiled to branches that split every MFMA pair into its own
+    // basic block.
+    auto src_of = [&](int kt) {
+      Src r{A, B, (int64_t)kt * KS};
+      if (SPLIT) {
+        const bool s1 = kt >= nk, s2 = kt >= 2 * nk;
+        r.a = A + (s2 ? dA2 : (s1 ? dA1 : 0));
+        r.b = B + (s2 ? dB2 : (s1 ? dB1 : 0));
+        r.k0 = (int64_t)(kt - (s2 ? 2 * nk : (s1 ? nk : 0))) * KS;
+      }
+      return r;
+    };
+    auto dma1 = [&](const Src &sr, int st, int q) {
       char *la = lds + st * 2 * OPB + wv * 64 * ROWB;
       const int j = q & 7;
-      if (q < 8) {
-        const char *a = A + (seg == 0 ? 0 : (seg == 1 ? dA1 : dA2));
-        __builtin_amdgcn_global_load_lds(a + (arow[j] + k0 + lchunk[j]) * 2, (lds_void *)(la + j * 8 * ROWB), 16, 0, 0);
-      } else {
-        const char *b = B + (seg == 0 ? 0 : (seg == 1 ? dB1 : dB2));
-        __builtin_amdgcn_global_load_lds(b + (brow[j] + k0 + lchunk[j]) * 2, (lds_void *)(la + OPB + j * 8 * ROWB),
+      if (q < 8)
+        __builtin_amdgcn_global_load_lds(sr.a + (arow[j] + sr.k0 + lchunk[j]) * 2, (lds_void *)(la + j * 8 * ROWB),
                                          16, 0, 0);
-      }
+      else
+        __builtin_amdgcn_global_load_lds(sr.b + (brow[j] + sr.k0 + lchunk[j]) * 2,
+                                         (lds_void *)(la + OPB + j * 8 * ROWB), 16, 0, 0);
     };
     // fragment read q of a k-step, in the order the next step's MFMA pairs
     // consume them: A0, B0, B1, B2, B3, A1, A2, A3
@@ -378,9 +396,9 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
     // one 16-deep k-step on fragment set `set`, in eight groups of an MFMA
     // pair, the fragment reads of the next step (RD: two in each of the first
     // two groups, one in each of the next four) and one DMA instruction per
-    // group (DMA: instructions q0 .. q0 + 7 of stage dkt into buffer dst);
-    // sched_barrier keeps the groups in this order
-    auto kstep = [&](int set, auto rd_, int rst, int rks, auto dma_, int dkt, int dst, int q0) {
+    // group (DMA: instructions q0 .. q0 + 7 of the stage at dsrc into buffer
+    // dst); sched_barrier keeps the groups in this order
+    auto kstep = [&](int set, auto rd_, int rst, int rks, auto dma_, const Src &dsrc, int dst, int q0) {
       constexpr bool RD = decltype(rd_)::value;
       constexpr bool DMA = decltype(dma_)::value;
 #pragma unroll
@@ -395,19 +413,24 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
           if (n < 2) { read1(set ^ 1, rst, rks, 2 * n); read1(set ^ 1, rst, rks, 2 * n + 1); }
           else if (n < 6) read1(set ^ 1, rst, rks, n + 2);
         }
-        if constexpr (DMA) dma1(dkt, dst, q0 + n);
+        if constexpr (DMA) dma1(dsrc, dst, q0 + n);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
     constexpr std::true_type yes{};
     constexpr std::false_type no{};
+    {
+      const Src s0 = src_of(0);
 #pragma unroll
-    for (int q = 0; q < 16; ++q) dma1(0, 0, q);
+      for (int q = 0; q < 16; ++q) dma1(s0, 0, q);
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (nkt > 1) {
+      const Src s1 = src_of(1);
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      if (nkt > 1) dma1(1, 1, q);
+      for (int q = 0; q < 8; ++q) dma1(s1, 1, q);
+    }
     read_frags(0, 0, 0);
     // One stage of the loop; DMAB / DMAA say whether stage kt+1 (B rows)
     // and stage kt+2 (A rows) exist.  The last two stages are peeled off
@@ -417,13 +440,14 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
     // waiting for loads nobody reads.
     auto body = [&](int kt, auto dmab, auto dmaa) {
       const int st = kt & 1;
-      kstep(0, yes, st, 1, dmab, kt + 1, st ^ 1, 8);   // B rows of stage kt+1
-      kstep(1, yes, st, 2, no, 0, 0, 0);
-      kstep(0, yes, st, 3, no, 0, 0, 0);
+      const Src nb = src_of(kt + 1), na = src_of(kt + 2);
+      kstep(0, yes, st, 1, dmab, nb, st ^ 1, 8);   // B rows of stage kt+1
+      kstep(1, yes, st, 2, no, nb, 0, 0);
+      kstep(0, yes, st, 3, no, nb, 0, 0);
       // stage kt+1 landed and every wave is done reading stage kt
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      kstep(1, yes, st ^ 1, 0, dmaa, kt + 2, st, 0);   // A rows of stage kt+2
+      kstep(1, yes, st ^ 1, 0, dmaa, na, st, 0);   // A rows of stage kt+2
     };
     int kt = 0;
     for (; kt < nkt - 2; ++kt) body(kt, yes, yes);
