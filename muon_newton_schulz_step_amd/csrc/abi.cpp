@@ -159,8 +159,27 @@ void step_patch(const muon_plan *p, char *h, const void *const *grads, float *co
   }
 }
 
+// The plan's second stream and its fork / join events, created once.
+static muon_status ensure_side(muon_plan *p) {
+  if (p->side_stream) return MUON_OK;
+  hipEvent_t f = nullptr, j = nullptr;
+  hipStream_t s2 = nullptr;
+  hipError_t e = hipEventCreateWithFlags(&f, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&j, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&s2, hipStreamNonBlocking);
+  if (e != hipSuccess) {
+    if (f) (void)hipEventDestroy(f);
+    if (j) (void)hipEventDestroy(j);
+    return hip_fail(e, "second stream");
+  }
+  p->fork_ev = f;
+  p->join_ev = j;
+  p->side_stream = s2;
+  return MUON_OK;
+}
+
 muon_status step_launch(muon_plan *p, const int32_t *skip_flag, float grad_scale, char *wsb, void *stream,
-                        bool timed) {
+                        bool timed, bool side) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   timed = timed && p->timing;
   if (timed) {
@@ -198,21 +217,45 @@ muon_status step_launch(muon_plan *p, const int32_t *skip_flag, float grad_scale
     if (p->opt.ns_steps == 0) {
       if ((e = launch_kc(probs, k1, np, wsb, scales, skip_flag, s)) != hipSuccess) return hip_fail(e, "copy launch");
     } else {
-      // large bf16 problems first (the bulk of the work), then small bf16
-      // ones, then fp32-operand ones
+      // Large bf16 problems first (the bulk of the work), then small bf16
+      // ones, then fp32-operand ones.  When a wave holds both large-tile and
+      // small-block groups, the small ones run on the second stream: their
+      // launches are short, mostly bound by HBM, and would otherwise wait
+      // for every large-tile launch; the groups share no buffer.
+      bool big_any = false, small_any = false;
+      for (int grp = 0; grp < NGROUPS; ++grp) {
+        if (W.tiles[grp][TL_MN128].empty()) continue;
+        (grp >= PG_BF16_BIG ? big_any : small_any) = true;
+      }
+      const bool fork = side && big_any && small_any;
+      hipStream_t s2 = s;
+      if (fork) {
+        muon_status st = ensure_side(p);
+        if (st != MUON_OK) return st;
+        s2 = static_cast<hipStream_t>(p->side_stream);
+        if ((e = hipEventRecord((hipEvent_t)p->fork_ev, s)) != hipSuccess) return hip_fail(e, "hipEventRecord (fork)");
+        if ((e = hipStreamWaitEvent(s2, (hipEvent_t)p->fork_ev, 0)) != hipSuccess)
+          return hip_fail(e, "hipStreamWaitEvent (fork)");
+      }
       for (int grp = NGROUPS - 1; grp >= PG_F32; --grp) {
         if (W.tiles[grp][TL_MN128].empty()) continue;
         const std::vector<Launch> &sched = p->schedule[grp];
+        hipStream_t sg = grp >= PG_BF16_BIG ? s : s2;
         for (const Launch &L : sched) {
           const bool big = grp >= PG_BF16_BIG && L.kind == Launch::GEMM_OP;
           const int list = big ? (L.mn ? TL_MN256 : TL_MM256) : (L.mn ? TL_MN128 : TL_MM128);
           const TileDev *tl = reinterpret_cast<const TileDev *>(wsb + W.off_tiles[grp][list]);
           const int nt = (int)W.tiles[grp][list].size();
           GemmArgs a{probs, tl, wsb, scales, L.r, skip_flag};
-          e = big ? launch_gemm256(a, nt, s) : launch_gemm(L.kind == Launch::GEMM_OP, a, nt, s);
+          e = big ? launch_gemm256(a, nt, sg) : launch_gemm(L.kind == Launch::GEMM_OP, a, nt, sg);
           if (e != hipSuccess) return hip_fail(e, "Newton-Schulz launch");
           ++ns_launches;
         }
+      }
+      if (fork) {
+        if ((e = hipEventRecord((hipEvent_t)p->join_ev, s2)) != hipSuccess) return hip_fail(e, "hipEventRecord (join)");
+        if ((e = hipStreamWaitEvent(s, (hipEvent_t)p->join_ev, 0)) != hipSuccess)
+          return hip_fail(e, "hipStreamWaitEvent (join)");
       }
     }
     if ((e = mark(wi, 2)) != hipSuccess) return hip_fail(e, "hipEventRecord (timing)");
@@ -255,7 +298,7 @@ muon_status muon_step_ex(muon_plan *p, const void *const *grads, float *const *m
   char *wsb = static_cast<char *>(ws);
   step_patch(p, h, grads, momenta, partitions, wsb);
   if ((st = upload(p, slot, ws, p->host_tables.size(), s)) != MUON_OK) return st;
-  if ((st = step_launch(p, skip_flag, grad_scale, wsb, stream, true)) != MUON_OK) return st;
+  if ((st = step_launch(p, skip_flag, grad_scale, wsb, stream, true, true)) != MUON_OK) return st;
   step_count(p, skip_flag, ws);
   return MUON_OK;
 }
@@ -466,6 +509,12 @@ muon_status muon_plan_phase_ms(muon_plan *p, float out[3], int32_t *ns_launches)
 
 void muon_plan_destroy(muon_plan *p) {
   if (!p) return;
+  if (p->side_stream) {
+    (void)hipStreamSynchronize((hipStream_t)p->side_stream);
+    (void)hipStreamDestroy((hipStream_t)p->side_stream);
+    (void)hipEventDestroy((hipEvent_t)p->fork_ev);
+    (void)hipEventDestroy((hipEvent_t)p->join_ev);
+  }
   for (void *ev : p->phase_events) (void)hipEventDestroy((hipEvent_t)ev);
   for (int s = 0; s < 2; ++s) {
     if (p->event_live[s]) (void)hipEventSynchronize((hipEvent_t)p->events[s]);

@@ -116,7 +116,7 @@ extern "C" muon_status muon_step_noalloc(muon_plan *p, const void *const *grads,
       return MUON_ERR_HIP;
     }
   }
-  st = muon::step_launch(p, skip_flag, grad_scale, wsb, stream, false);
+  st = muon::step_launch(p, skip_flag, grad_scale, wsb, stream, false, false);
   if (st != MUON_OK) return st;
   muon::step_count(p, skip_flag, wsb);
   return MUON_OK;

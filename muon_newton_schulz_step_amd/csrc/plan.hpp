@@ -105,6 +105,11 @@ struct muon_plan {
   void *events[2] = {nullptr, nullptr};
   bool event_live[2] = {false, false};
   int slot = 0;
+  // a second stream (default priority) on which the small-block problem
+  // groups run beside the large-tile ones, with the fork / join events;
+  // created on the first step that has both kinds
+  void *side_stream = nullptr;
+  void *fork_ev = nullptr, *join_ev = nullptr;
   // phase timing (events created lazily; 4 per wave: start, K1 done, NS done, K3 done)
   bool timing = false;
   bool timed_step = false;
@@ -122,13 +127,14 @@ muon_status build_plan(muon_plan *p);
 //    (p->host_tables.size() bytes) for a workspace at wsb;
 //  - step_launch: K1, the norm, the Newton-Schulz launches and K3 on stream
 //    s, reading the tables at the head of the workspace (timed: record the
-//    phase events if timing is enabled);
+//    phase events if timing is enabled; side: run the small-block groups on
+//    the plan's second stream, concurrently with the large-tile groups);
 //  - step_count: the plan's counters.
 muon_status step_check(muon_plan *p, const void *const *grads, float *const *momenta, float *const *partitions,
                        const int32_t *skip_flag, float grad_scale, void *ws, size_t ws_bytes);
 void step_patch(const muon_plan *p, char *h, const void *const *grads, float *const *momenta,
                 float *const *partitions, char *wsb);
 muon_status step_launch(muon_plan *p, const int32_t *skip_flag, float grad_scale, char *wsb, void *stream,
-                        bool timed);
+                        bool timed, bool side);
 void step_count(muon_plan *p, const int32_t *skip_flag, const void *ws);
 }
