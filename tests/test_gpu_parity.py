@@ -271,6 +271,37 @@ def test_deterministic_and_wave_invariant():
             np.testing.assert_array_equal(a, b)
 
 
+@pytest.mark.parametrize("method,cap", [("standard", 5 << 20), ("gram", 8 << 20)])
+def test_mixed_sizes_waves_and_second_stream_bitwise(method, cap):
+    # large-tile problems (m >= 256) beside small-block ones (head blocks,
+    # m < 256, fp32-operand blocks): the small groups run on the plan's
+    # second stream, joined before the writeback.  Capped, the group runs in
+    # three workspace waves, two of which hold both kinds (a fork and a join
+    # per wave); one wave and three give the same bits, and the one-wave run
+    # matches the oracle.
+    shapes = [(512, 700), (300, 200), (260, 300), (1024, 256), (600, 280), (64, 900), (33, 65)]
+    heads = [0, 0, 0, 8, 0, 0, 0]
+    offsets, P = O.pack_layout(shapes, 2, 16)
+    micro = _micro(shapes, "bf16", 0.02, 1, 2, cid=61)
+    outs = []
+    for c in (0, cap):
+        g = M.MuonGroup(shapes, heads=heads, offsets=offsets, num_partitions=2, partition_numel=P, method=method,
+                        precision="bf16", grad_dtype="bf16", max_inflight_bytes=c)
+        waves = {}
+        for q in g.problems():
+            waves.setdefault(q["wave"], set()).add(q["m"] >= 256)
+        assert len(waves) == (1 if c == 0 else 3)
+        assert sum(1 for kinds in waves.values() if len(kinds) == 2) == (1 if c == 0 else 2)
+        parts, moms = run_steps(g, micro, "bf16", use_accumulate=False)
+        outs.append((parts, moms))
+    for a, b in zip(outs[0][0] + outs[0][1], outs[1][0] + outs[1][1]):
+        np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
+    res, state = _oracle_run(shapes, heads, offsets, 2, P, micro, "bf16", method)
+    _compare(shapes, offsets, outs[0][0], res, TOL["bf16"], f"mixed/{method}")
+    _check_padding(outs[0][0], shapes, offsets, P)
+    _check_momentum(outs[0][1], state, res)
+
+
 def test_per_head_toggle_changes_only_tagged():
     shapes = [(256, 128), (128, 384)]
     micro = _micro(shapes, "bf16", 0.02, 1, 1, cid=31)
