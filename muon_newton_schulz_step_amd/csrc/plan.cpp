@@ -500,16 +500,17 @@ muon_status build_plan(muon_plan *p) {
         if (d.off[r] >= 0) d.off[r] += p->data_off;
     for (auto &k : W.k1) { k.orig_off += p->data_off; k.trans_off += p->data_off; }
   }
-  // serialize
+  // serialize (an empty table has no data pointer to copy from)
   p->host_tables.assign(p->tables_bytes, 0);
+  auto put = [&](int64_t off, const auto &v) {
+    if (!v.empty()) std::memcpy(p->host_tables.data() + off, v.data(), v.size() * sizeof(v[0]));
+  };
   for (auto &W : p->waves) {
-    char *h = p->host_tables.data();
-    std::memcpy(h + W.off_prob, W.probs.data(), W.probs.size() * sizeof(ProbDev));
-    std::memcpy(h + W.off_k1, W.k1.data(), W.k1.size() * sizeof(K1Prob));
+    put(W.off_prob, W.probs);
+    put(W.off_k1, W.k1);
     for (int g = 0; g < NGROUPS; ++g)
-      for (int l = 0; l < NLISTS; ++l)
-        std::memcpy(h + W.off_tiles[g][l], W.tiles[g][l].data(), W.tiles[g][l].size() * sizeof(TileDev));
-    std::memcpy(h + W.off_runs, W.runs.data(), W.runs.size() * sizeof(K3Run));
+      for (int l = 0; l < NLISTS; ++l) put(W.off_tiles[g][l], W.tiles[g][l]);
+    put(W.off_runs, W.runs);
   }
   return MUON_OK;
 }
