@@ -75,7 +75,10 @@ typedef enum { MUON_NS_STANDARD = 0, MUON_NS_GRAM = 1 } muon_ns_method;
  * throughout.  BF16: bf16 MFMA operands with fp32 accumulation; the Gram
  * form's small-side chain (R, P, Q) is fp32 for blocks with m < 256 and a
  * split-bf16 pair (hi + lo, three bf16 products per product) for m >= 256,
- * except that blocks with m >= 2048 accumulate Q with one bf16 product. */
+ * except that blocks with m >= 2048 accumulate Q with one bf16 product.
+ * Blocks with 64 <= m <= 128 (either form) run their whole iteration in one
+ * workgroup; there the Gram form's output product takes Q as a bf16 pair
+ * (hi + lo) rather than its bf16 value. */
 typedef enum { MUON_PREC_FP32 = 0, MUON_PREC_BF16 = 1 } muon_ns_precision;
 
 /* Storage type of a gradient or update buffer. */

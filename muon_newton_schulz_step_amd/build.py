@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB_NAME = "libmuon_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["plan.cpp", "abi.cpp", "noalloc.hip", "k_elem.hip", "k_gemm.hip", "k_gemm256.hip"]
+SOURCES = ["plan.cpp", "abi.cpp", "noalloc.hip", "k_elem.hip", "k_gemm.hip", "k_gemm256.hip", "k_head.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.

@@ -241,6 +241,16 @@ muon_status step_launch(muon_plan *p, const int32_t *skip_flag, float grad_scale
         if (W.tiles[grp][TL_MN128].empty()) continue;
         const std::vector<Launch> &sched = p->schedule[grp];
         hipStream_t sg = grp >= PG_BF16_BIG ? s : s2;
+        if (grp == PG_HEAD) {
+          // one workgroup per block runs its whole iteration
+          const TileDev *tl = reinterpret_cast<const TileDev *>(wsb + W.off_tiles[grp][TL_MN128]);
+          HeadArgs ha{probs, tl, wsb, scales, skip_flag, p->opt.a, p->opt.b, p->opt.c, p->opt.ns_steps,
+                      p->opt.method == MUON_NS_STANDARD ? 1 : 0};
+          if ((e = launch_head(ha, (int)W.tiles[grp][TL_MN128].size(), sg)) != hipSuccess)
+            return hip_fail(e, "Newton-Schulz launch (fused blocks)");
+          ++ns_launches;
+          continue;
+        }
         for (const Launch &L : sched) {
           const bool big = grp >= PG_BF16_BIG && L.kind == Launch::GEMM_OP;
           const int list = big ? (L.mn ? TL_MN256 : TL_MM256) : (L.mn ? TL_MN128 : TL_MM128);

@@ -42,6 +42,20 @@ struct GemmArgs {
   const int32_t *skip;   // may be NULL; non-zero: the launch does nothing
 };
 hipError_t launch_gemm(bool bf16_operands, const GemmArgs &a, int ntiles, hipStream_t s);
+
+// The fused Newton-Schulz of the PG_HEAD blocks: one workgroup per entry of
+// the tile list (its tm, tn are 0) runs the block's whole iteration.
+struct HeadArgs {
+  const ProbDev *probs;
+  const TileDev *tiles;
+  char *ws;
+  const float *scales;
+  const int32_t *skip;   // may be NULL; non-zero: the launch does nothing
+  float a, b, c;
+  int32_t steps;         // >= 1
+  int32_t standard;      // 1: standard form, 0: Gram form
+};
+hipError_t launch_head(const HeadArgs &a, int nprob, hipStream_t s);
 hipError_t launch_gemm256(const GemmArgs &a, int ntiles, hipStream_t s);
 
 }  // namespace muon

@@ -293,9 +293,19 @@ muon_status build_plan(muon_plan *p) {
   auto split_chain = [&](const ProblemPlan &q) {
     return !standard && !p->mats[q.matrix].ops32 && q.m >= BIG_TILE_MIN_M;
   };
+  // blocks whose whole iteration runs in one workgroup: no m x m buffers
+  auto fused = [&](const ProblemPlan &q) {
+    return o.ns_steps > 0 && !p->mats[q.matrix].ops32 && q.m <= HEAD_MAX_M;
+  };
+  // Parity of the original-layout X copy that U aliases: one the matrix's
+  // last Newton-Schulz reads do not touch.  The fused blocks read only
+  // parity 0 (the workgroups of a matrix's head blocks run at different
+  // times, so U may not alias anything any of them reads).
+  auto u_parity = [&](const MatrixPlan &M) { return fused(p->probs[M.prob0]) ? 1 : upar; };
   auto problem_bytes = [&](const ProblemPlan &q) {
     const int64_t e = p->mats[q.matrix].elem;
     int64_t mm = q.m * q.ldm;
+    if (fused(q)) return (int64_t)0;
     if (standard) return 2 * rup(mm * e, kAlign);
     if (split_chain(q)) return 10 * rup(mm * 2, kAlign);
     return 5 * rup(mm * 4, kAlign) + (e == 2 ? rup(mm * 2, kAlign) : 0);
@@ -343,7 +353,10 @@ muon_status build_plan(muon_plan *p) {
         ProblemPlan &q = p->probs[M.prob0 + h];
         int64_t mm = q.m * q.ldm;
         std::fill(q.lo_off, q.lo_off + 5, -1);
-        if (standard) {
+        std::fill(q.mm_off, q.mm_off + 6, -1);
+        if (fused(q)) {
+          // R, P and Q stay on the CU
+        } else if (standard) {
           q.mm_off[0] = dat.take(mm * e);
           q.mm_off[1] = dat.take(mm * e);
         } else if (split_chain(q)) {
@@ -405,7 +418,7 @@ muon_status build_plan(muon_plan *p) {
       // of X that the last Newton-Schulz launch does not read: parity T&1 of
       // the standard form (the final launch reads parity (T-1)&1), parity 1
       // for the Gram form and for zero steps (both read only parity 0).
-      d.off[R_U] = M.orig_off[upar] + (int64_t)q.head * M.hr * M.desc.cols * e;
+      d.off[R_U] = M.orig_off[u_parity(M)] + (int64_t)q.head * M.hr * M.desc.cols * e;
       d.ld[R_U] = (int32_t)M.desc.cols;
       W.probs.push_back(d);
 
@@ -427,6 +440,7 @@ muon_status build_plan(muon_plan *p) {
       W.k1_matrix.push_back(q.matrix);
 
       const int grp = M.ops32 ? PG_F32
+                      : fused(q) ? PG_HEAD
                       : q.m < BIG_TILE_MIN_M ? PG_BF16
                       : (!standard && q.m >= GRAM_LEAN_MIN_M) ? PG_BF16_LEAN : PG_BF16_BIG;
       // Tiles of a problem in 4 x 8 blocks (block-row-major, row-major inside
@@ -446,7 +460,8 @@ muon_status build_plan(muon_plan *p) {
               for (int64_t b = B0; b < std::min(B0 + BC, tnn); ++b)
                 W.tiles[grp][lmn].push_back(TileDev{(int32_t)li, (int16_t)a, (int16_t)b});
       };
-      add_tiles(GEMM_TILE, TL_MM128, TL_MN128);
+      if (grp == PG_HEAD) W.tiles[grp][TL_MN128].push_back(TileDev{(int32_t)li, 0, 0});
+      else add_tiles(GEMM_TILE, TL_MM128, TL_MN128);
       if (grp >= PG_BF16_BIG) add_tiles(BIG_TILE, TL_MM256, TL_MN256);
     }
     W.k1_tiles = k1t;
@@ -493,7 +508,7 @@ muon_status build_plan(muon_plan *p) {
   p->data_off = ws.take(max_data);
   p->ws_bytes = rup(ws.top, kAlign);
   // absolute offsets inside the workspace
-  for (auto &M : p->mats) M.u_off = p->data_off + M.orig_off[upar];
+  for (auto &M : p->mats) M.u_off = p->data_off + M.orig_off[u_parity(M)];
   for (auto &W : p->waves) {
     for (auto &d : W.probs)
       for (int r = 0; r < NROLES; ++r)

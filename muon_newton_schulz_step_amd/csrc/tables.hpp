@@ -37,11 +37,18 @@ constexpr int BIG_TILE = 256;
 #endif
 constexpr int BIG_TILE_MIN_M = MUON_BIG_TILE_MIN_M;
 
-// Problem groups of a wave: fp32 operands; bf16 with m < BIG_TILE; bf16 with
-// m >= BIG_TILE; and, in the Gram form only, bf16 blocks with
+// Problem groups of a wave: fp32 operands; bf16 with m < BIG_TILE; bf16
+// blocks fused into one workgroup each (below); bf16 with m >= BIG_TILE;
+// and, in the Gram form only, bf16 blocks with
 // m >= GRAM_LEAN_MIN_M, whose chain accumulates Q with one bf16 product
 // (below).  Tile lists per group: m x m and m x n, at each tile size.
-enum ProbGroup : int { PG_F32 = 0, PG_BF16 = 1, PG_BF16_BIG = 2, PG_BF16_LEAN = 3, NGROUPS };
+enum ProbGroup : int { PG_F32 = 0, PG_BF16 = 1, PG_HEAD = 2, PG_BF16_BIG = 3, PG_BF16_LEAN = 4, NGROUPS };
+
+// bf16 blocks with m <= this (at least BF16_MIN_M, below), either form, at
+// least one step: the whole iteration of a block runs in one workgroup
+// (PG_HEAD; its tile list holds one entry per block, and the group has no
+// launch schedule).
+constexpr int HEAD_MAX_M = 128;
 
 // Gram form, bf16 blocks with m >= this: Q <- P Q is one bf16 product of
 // the high halves, stored as bf16 (three-segment split products for the

@@ -11,7 +11,9 @@
 //     checked to lie inside the X copy it aliases instead);
 //   - every tile of every tile list lies inside its problem, symmetric lists
 //     hold upper-triangle tiles only, and 256-tile lists belong to problems
-//     with m >= 256;
+//     with m >= 256; the blocks fused into one workgroup each are exactly
+//     the bf16 blocks with 64 <= m <= 128 (at least one step), listed once,
+//     with no m x m buffer, no tile elsewhere and U apart from what they read;
 //   - every K1 entry covers its block, every owned run lies inside its
 //     matrix and its partition, the chunk prefixes count the chunks exactly;
 //   - the serialized tables fit their region and the scratch sums follow it.
@@ -148,6 +150,43 @@ void check_plan(const muon_plan *p, uint64_t it) {
           if (T == BIG_TILE && d.m < BIG_TILE_MIN_M) fail("large tile on a small problem", it);
         }
       }
+    // fused blocks (bf16, 64 <= m <= 128, at least one step): one entry each
+    // in the fused group's list, X0 in both layouts and U allocated, U not
+    // aliasing the parity-0 copy they read, no m x m buffer, and no tile in
+    // any other list
+    {
+      std::vector<int> fused(W.probs.size(), 0), tiled(W.probs.size(), 0);
+      for (const TileDev &t : W.tiles[PG_HEAD][TL_MN128]) {
+        if (t.prob < 0 || t.prob >= (int)W.probs.size()) continue;
+        ++fused[t.prob];
+        if (t.tm != 0 || t.tn != 0) fail("fused entry with a tile position", it);
+      }
+      if (!W.tiles[PG_HEAD][TL_MM128].empty() || !W.tiles[PG_HEAD][TL_MM256].empty() ||
+          !W.tiles[PG_HEAD][TL_MN256].empty())
+        fail("fused group with tile lists", it);
+      for (int g = 0; g < NGROUPS; ++g)
+        for (int l = 0; l < NLISTS; ++l)
+          if (g != PG_HEAD)
+            for (const TileDev &t : W.tiles[g][l])
+              if (t.prob >= 0 && t.prob < (int)W.probs.size()) ++tiled[t.prob];
+      for (size_t pi = 0; pi < W.probs.size(); ++pi) {
+        const ProbDev &d = W.probs[pi];
+        const MatrixPlan &M = p->mats[d.matrix];
+        const bool want = p->opt.ns_steps > 0 && !M.ops32 && d.m <= HEAD_MAX_M;
+        if (want != (fused[pi] > 0)) fail("fused group membership", it);
+        if (fused[pi] > 1) fail("fused block listed twice", it);
+        if (fused[pi] && tiled[pi]) fail("fused block also tiled", it);
+        if (!fused[pi] && !tiled[pi]) fail("block in no list", it);
+        if (fused[pi]) {
+          if (d.m < BF16_MIN_M) fail("fused block below the bf16 minimum", it);
+          if (d.off[R_XR0] < 0 || d.off[R_XC0] < 0 || d.off[R_U] < 0) fail("fused block without X0 or U", it);
+          for (int r = R_MA; r <= R_QB; ++r)
+            if (d.off[r] >= 0) fail("fused block with an m x m buffer", it);
+          const int64_t lo0 = p->data_off + M.orig_off[0], hi0 = lo0 + M.desc.rows * M.ldc * M.elem;
+          if (d.off[R_U] >= lo0 && d.off[R_U] < hi0) fail("fused block's U aliases the copy it reads", it);
+        }
+      }
+    }
     // K1 entries
     int32_t k1t = 0;
     for (const K1Prob &k : W.k1) {

@@ -271,7 +271,7 @@ def test_deterministic_and_wave_invariant():
             np.testing.assert_array_equal(a, b)
 
 
-@pytest.mark.parametrize("method,cap", [("standard", 5 << 20), ("gram", 8 << 20)])
+@pytest.mark.parametrize("method,cap", [("standard", 4 << 20), ("gram", 6 << 20)])
 def test_mixed_sizes_waves_and_second_stream_bitwise(method, cap):
     # large-tile problems (m >= 256) beside small-block ones (head blocks,
     # m < 256, fp32-operand blocks): the small groups run on the plan's
