@@ -242,6 +242,10 @@ muon_status muon_step_ex(muon_plan *p, const void *const *grads, float *const *m
  *   - The update-norm partials it leaves stay in the array, so
  *     muon_apply_update cannot follow it (it reports that no step ran on its
  *     workspace); run muon_step_ex when the parameter update follows.
+ *   - It enqueues kernels only (no copy, memset or event), so it can be
+ *     captured into a graph on a capturing stream: the tables travel in the
+ *     captured kernel arguments and each replay uploads them again.  The
+ *     plan's counters (muon_plan_stats) count the capture, not the replays.
  * Errors: WORKSPACE if the plan's workspace (muon_plan_workspace_bytes)
  * exceeds MUON_NOALLOC_SCRATCH_BYTES (max_inflight_bytes can cut it into
  * waves that fit); UNSUPPORTED if its tables exceed 96 KB; then as

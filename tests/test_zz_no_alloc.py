@@ -5,7 +5,9 @@ The two entry points launch the same kernels on the same inputs, so their
 momenta and partitions must agree bit for bit.  Calls come in a row on one
 process: a group, then a smaller group (the array keeps the first call's
 contents), then the first group again in the Gram form, then a discarded
-step (device skip flag) and a loss-scaled one.
+step (device skip flag) and a loss-scaled one.  Last, the step captured once
+into a graph and replayed on new gradients, with eager steps between the
+replays: every replay equals an eager step on the same inputs.
 """
 
 from __future__ import annotations
@@ -99,4 +101,50 @@ def test_noalloc_refuses_a_plan_beyond_the_array(torch):
         g.step_noalloc(grads, moms, parts)
     assert ei.value.name == "MUON_ERR_WORKSPACE"
     assert g.stats()["steps"] == 0
+    g.close()
+
+
+def test_noalloc_step_replays_from_a_graph(torch):
+    # A graph is what a caller that cannot allocate records: the step's
+    # launches (tables included, as kernel arguments) are captured once and
+    # replayed; each replay re-uploads the captured tables into the array.
+    shapes = [(300, 200), (128, 640), (512, 700), (17, 13)]
+    offsets, P = O.pack_layout(shapes, 2, 16)
+    g = M.MuonGroup(shapes, offsets=offsets, num_partitions=2, partition_numel=P, method="standard",
+                    precision="bf16", grad_dtype="bf16")
+    assert g.workspace_bytes <= M._lib.NOALLOC_SCRATCH_BYTES
+    grads = [torch.empty(s, dtype=torch.bfloat16, device="cuda:0") for s in shapes]
+    moms = [to_device(W.warm_momentum(s, 800 + i, 0.02), "fp32").reshape(s) for i, s in enumerate(shapes)]
+    parts = sentinel_partitions(2, P)
+
+    def load_grads(k):
+        for i, s in enumerate(shapes):
+            grads[i].copy_(to_device(W.make_grad(s, 900 + 10 * k + i, 0.02, "bf16"), "bf16").reshape(s))
+
+    # eager warm-up on a side stream, then capture on the graph's stream
+    load_grads(0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        g.step_noalloc(grads, moms, parts)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g.step_noalloc(grads, moms, parts)
+    torch.cuda.synchronize()
+    for k in range(1, 4):
+        load_grads(k)
+        torch.cuda.synchronize()
+        # the eager step on copies of the same state and inputs
+        ref_grads = [x.clone() for x in grads]
+        ref_moms = [m.clone() for m in moms]
+        ref_parts = [p.clone() for p in parts]
+        g.step_noalloc(ref_grads, ref_moms, ref_parts)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _equal(([host(p) for p in ref_parts], [host(m) for m in ref_moms]),
+               ([host(p) for p in parts], [host(m) for m in moms]), f"replay {k}")
+    graph.reset()
     g.close()
