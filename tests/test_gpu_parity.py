@@ -34,7 +34,7 @@ def _cuda():
 
 
 def _oracle_run(shapes, heads, offsets, R, P, micro, micro_dtype, method, steps_ns=5, nesterov=True,
-                momenta0=None, beta=0.95):
+                momenta0=None, beta=0.95, coeffs=O.NS_COEFFS):
     """Run the oracle over the same micro-batches.  Also returns, per matrix,
     the largest |beta m_prev| + |(1-beta) g| seen over the steps: the scale of
     the terms whose fp32 evaluation the momentum check bounds."""
@@ -42,7 +42,7 @@ def _oracle_run(shapes, heads, offsets, R, P, micro, micro_dtype, method, steps_
     if momenta0 is not None:
         state.momenta = [m.astype(np.float32).copy() for m in momenta0]
     b = float(np.float32(beta))
-    opt = O.MuonOptions(beta=b, nesterov=nesterov, method=method, steps=steps_ns,
+    opt = O.MuonOptions(beta=b, nesterov=nesterov, method=method, steps=steps_ns, coeffs=coeffs,
                         eps=float(np.float32(O.NORM_EPS)))
     res = None
     sentinel = np.array([SENTINEL], dtype=np.uint32).view(np.float32)[0]
@@ -163,6 +163,23 @@ def test_ns_step_counts(steps_ns, method, precision):
     parts, _ = run_steps(g, micro, "fp32", use_accumulate=False)
     res, _ = _oracle_run(shapes, [0, 0, 0], offsets, 1, P, micro, "fp32", method, steps_ns=steps_ns)
     _compare(shapes, offsets, parts, res, TOL[precision], f"T={steps_ns}/{method}/{precision}")
+
+
+@pytest.mark.parametrize("precision", ["fp32", "bf16"])
+@pytest.mark.parametrize("method", ["standard", "gram"])
+def test_custom_coefficients_and_step_count(method, precision):
+    # (a, b, c) and the step count come from the options: the quintic
+    # 2x - 1.5x^3 + 0.5x^5 over 7 steps, on every kernel kind (a large-tile
+    # block, two fused ones, an fp32-operand one)
+    shapes = [(300, 520), (128, 700), (96, 96), (40, 90)]
+    coeffs = (2.0, -1.5, 0.5)
+    offsets, P = O.pack_layout(shapes, 1, 16)
+    g = M.MuonGroup(shapes, method=method, precision=precision, grad_dtype="fp32", ns_steps=7, coeffs=coeffs)
+    micro = _micro(shapes, "fp32", 1.0, 1, 1, cid=13)
+    parts, _ = run_steps(g, micro, "fp32", use_accumulate=False)
+    res, _ = _oracle_run(shapes, [0] * len(shapes), offsets, 1, P, micro, "fp32", method, steps_ns=7,
+                         coeffs=coeffs)
+    _compare(shapes, offsets, parts, res, TOL[precision], f"coeffs/{method}/{precision}")
 
 
 def test_nesterov_off_and_beta():
