@@ -271,12 +271,15 @@ def test_accumulate_bit_exact_fp32_sequence():
             np.testing.assert_array_equal(host(accs[i]), want)
 
 
-def test_deterministic_and_wave_invariant():
+@pytest.mark.parametrize("method", ["standard", "gram"])
+def test_deterministic_and_wave_invariant(method):
+    # 128-tile, fused (128 x 128) and large-tile-free blocks; run twice and in
+    # one wave per matrix: the same bits
     shapes = [(200, 300), (300, 200), (128, 128), (64, 512)]
     micro = _micro(shapes, "bf16", 0.02, 1, 1, cid=21)
     outs = []
     for cap in (0, 0, 1):
-        g = M.MuonGroup(shapes, heads=[0, 0, 0, 2], precision="bf16", grad_dtype="bf16",
+        g = M.MuonGroup(shapes, heads=[0, 0, 0, 2], precision="bf16", grad_dtype="bf16", method=method,
                         max_inflight_bytes=cap)
         if cap:
             assert g.stats()["waves"] == len(shapes)
