@@ -209,6 +209,9 @@ def main() -> int:
                          "headline is the standard one (0: no Gram leg)")
     ap.add_argument("--max-inflight-gb", type=float, default=0.0,
                     help="cap the Newton-Schulz workspace at this many GB (the group then runs in waves)")
+    ap.add_argument("--schedule", default="launches", choices=["launches", "persistent"],
+                    help="Newton-Schulz schedule of the large-tile blocks: one launch per product, or one "
+                         "persistent launch per wave with per-block dependency counters")
     ap.add_argument("--calibrate-copy", type=float, default=0.0,
                     help="only copy this many GiB device-to-device (a plain copy of known size, the reference "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -245,7 +248,7 @@ def main() -> int:
     def make_group(meth):
         return M.MuonGroup(wl.shapes, heads=wl.heads, offsets=offsets, num_partitions=wl.num_partitions,
                            partition_numel=P, method=meth, precision=args.precision, grad_dtype=step_dtype,
-                           max_inflight_bytes=cap)
+                           max_inflight_bytes=cap, schedule=args.schedule)
 
     g = make_group(method)
     log(f"workload {wl.name}: {len(wl.shapes)} matrices, {wl.numel / 1e9:.3f} G elements, method {method}, "
@@ -380,7 +383,7 @@ def main() -> int:
         "config": {"workload": wl.name, "matrices": len(wl.shapes), "numel": numel, "gas": wl.gas,
                    "partitions": wl.num_partitions, "ns_method": method, "ns_steps": g.options.ns_steps,
                    "ns_precision": args.precision, "grad_dtype": step_dtype, "workspace_gb": round(ws_gb, 1),
-                   "waves": waves},
+                   "waves": waves, "ns_schedule": args.schedule},
         "phases_ms": {"k1_norm": round(k1_ms, 3), "newton_schulz": round(ns_ms, 3), "k3_scatter": round(k3_ms, 3),
                       "accumulate": round(statistics.mean(acc_ms), 3) if acc is not None else None,
                       "apply_update": round(statistics.mean(apply_ms), 3)},

@@ -81,6 +81,19 @@ typedef enum { MUON_NS_STANDARD = 0, MUON_NS_GRAM = 1 } muon_ns_method;
  * (hi + lo) rather than its bf16 value. */
 typedef enum { MUON_PREC_FP32 = 0, MUON_PREC_BF16 = 1 } muon_ns_precision;
 
+/* How the Newton-Schulz products of blocks with m >= 256 (bf16) are put on
+ * the device.  LAUNCHES: one launch per product of the schedule over every
+ * such block of a wave.  PERSISTENT: one launch per wave runs every product
+ * of every such block: a workgroup per CU takes tiles from a queue of its
+ * XCD, each block's products stay on one XCD, and a tile starts once its
+ * block's previous product is complete (a counter per block), so no
+ * device-wide barrier separates the products.  Results are bitwise those
+ * of LAUNCHES.  PERSISTENT falls back to LAUNCHES on a device that does not
+ * have 8 XCDs of 32 CUs.  Neither form is fixed by the pages, which run the
+ * products as framework matmuls; LAUNCHES is the faster one on MI355X for
+ * the groups measured, and is the default. */
+typedef enum { MUON_SCHED_LAUNCHES = 0, MUON_SCHED_PERSISTENT = 1 } muon_ns_schedule;
+
 /* Storage type of a gradient or update buffer. */
 typedef enum { MUON_DT_FP32 = 0, MUON_DT_BF16 = 1 } muon_dtype;
 
@@ -107,6 +120,8 @@ typedef struct {
   int32_t precision;   /* muon_ns_precision                                */
   int32_t grad_dtype;  /* muon_dtype of the grads given to muon_step       */
   uint64_t max_inflight_bytes; /* cap on the workspace; 0 = no cap          */
+  int32_t schedule;    /* muon_ns_schedule                                 */
+  int32_t reserved;    /* must be 0                                        */
 } muon_options;
 
 typedef struct {
@@ -156,7 +171,7 @@ typedef struct muon_plan muon_plan;
 
 /* Default options: beta 0.95, Nesterov on, standard form, 5 steps,
  * (a,b,c) = (3.4445, -4.7750, 2.0315), eps 1e-7, bf16 precision, bf16
- * grads, no workspace cap.  Errors: INVALID_ARG if out is NULL. */
+ * grads, no workspace cap, one launch per product.  Errors: INVALID_ARG if out is NULL. */
 muon_status muon_default_options(muon_options *out);
 
 /* Build a plan for a group of n matrices (host only; no device call).

@@ -9,7 +9,7 @@ Device memory and streams come from the caller (e.g. torch tensors).
 from __future__ import annotations
 
 from . import _lib
-from ._lib import (DTYPE, EXPORTS, NS_METHOD, PRECISION, MuonError, load, muon_accumulate,  # noqa: F401
+from ._lib import (DTYPE, EXPORTS, NS_METHOD, PRECISION, SCHEDULE, MuonError, load, muon_accumulate,  # noqa: F401
                    muon_apply_update, muon_check_finite, muon_default_options, muon_last_error, muon_layout,
                    muon_plan_create, muon_plan_destroy, muon_plan_phase_ms, muon_plan_problems, muon_plan_runs,
                    muon_plan_set_timing, muon_plan_stats, muon_plan_workspace_bytes, muon_scatter,
@@ -69,7 +69,7 @@ class MuonGroup:
     def __init__(self, shapes, heads=None, offsets=None, num_partitions: int = 1, partition_numel=None,
                  align: int = 16, method: str = "standard", precision: str = "bf16", grad_dtype: str = "bf16",
                  ns_steps: int = 5, beta: float = 0.95, nesterov: bool = True, coeffs=None, eps=None,
-                 max_inflight_bytes: int = 0):
+                 max_inflight_bytes: int = 0, schedule: str = "launches"):
         self.shapes = [(int(r), int(c)) for r, c in shapes]
         self.heads = list(heads) if heads is not None else [0] * len(self.shapes)
         if offsets is None or partition_numel is None:
@@ -94,6 +94,7 @@ class MuonGroup:
         o.precision = PRECISION[precision]
         o.grad_dtype = DTYPE[grad_dtype]
         o.max_inflight_bytes = int(max_inflight_bytes)
+        o.schedule = SCHEDULE[schedule]
         self.options = o
         lay = muon_layout(self.partition_numel, self.num_partitions, 0)
         mats = [(r, c, h, off) for (r, c), h, off in zip(self.shapes, self.heads, self.offsets)]

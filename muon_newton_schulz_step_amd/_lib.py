@@ -23,6 +23,7 @@ STATUS = {0: "MUON_OK", 1: "MUON_ERR_INVALID_ARG", 2: "MUON_ERR_UNSUPPORTED", 3:
 NS_METHOD = {"standard": 0, "gram": 1}
 PRECISION = {"fp32": 0, "bf16": 1}
 DTYPE = {"fp32": 0, "bf16": 1}
+SCHEDULE = {"launches": 0, "persistent": 1}
 
 # every symbol include/muon.h declares
 EXPORTS = ("muon_default_options", "muon_plan_create", "muon_plan_workspace_bytes", "muon_accumulate",
@@ -39,7 +40,8 @@ class muon_matrix(C.Structure):
 class muon_options(C.Structure):
     _fields_ = [("beta", C.c_float), ("nesterov", C.c_int32), ("method", C.c_int32), ("ns_steps", C.c_int32),
                 ("a", C.c_float), ("b", C.c_float), ("c", C.c_float), ("eps", C.c_float),
-                ("precision", C.c_int32), ("grad_dtype", C.c_int32), ("max_inflight_bytes", C.c_uint64)]
+                ("precision", C.c_int32), ("grad_dtype", C.c_int32), ("max_inflight_bytes", C.c_uint64),
+                ("schedule", C.c_int32), ("reserved", C.c_int32)]
 
 
 class muon_layout(C.Structure):

@@ -178,6 +178,16 @@ static muon_status ensure_side(muon_plan *p) {
   return MUON_OK;
 }
 
+// The persistent schedule assumes 8 XCDs of 32 CUs, one workgroup each,
+// with workgroup i on XCD i mod 8 (true of MI355X with all its CUs in one
+// partition); on any other device the step falls back to the launches.
+static bool persistent_fits() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
+  return cus == PQ_XCDS * 32;
+}
+
 muon_status step_launch(muon_plan *p, const int32_t *skip_flag, float grad_scale, char *wsb, void *stream,
                         bool timed, bool side) {
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -237,10 +247,26 @@ muon_status step_launch(muon_plan *p, const int32_t *skip_flag, float grad_scale
         if ((e = hipStreamWaitEvent(s2, (hipEvent_t)p->fork_ev, 0)) != hipSuccess)
           return hip_fail(e, "hipStreamWaitEvent (fork)");
       }
+      const bool persist = p->opt.schedule == MUON_SCHED_PERSISTENT && persistent_fits();
       for (int grp = NGROUPS - 1; grp >= PG_F32; --grp) {
         if (W.tiles[grp][TL_MN128].empty()) continue;
         const std::vector<Launch> &sched = p->schedule[grp];
         hipStream_t sg = grp >= PG_BF16_BIG ? s : s2;
+        if (persist && !W.pq[grp].empty()) {
+          // every product of every problem of the group in one launch
+          PersistArgs pa;
+          pa.probs = probs; pa.ws = wsb; pa.scales = scales; pa.skip = skip_flag;
+          pa.launches = reinterpret_cast<const PLaunch *>(wsb + W.off_pl[grp]);
+          pa.items = reinterpret_cast<const TileDev *>(wsb + W.off_pq[grp]);
+          pa.ntl = reinterpret_cast<const int32_t *>(wsb + W.off_pntl);
+          pa.counters = reinterpret_cast<int32_t *>(wsb + W.off_pcnt[grp]);
+          for (int x = 0; x <= PQ_XCDS; ++x) pa.qoff[x] = W.pq_off[grp][x];
+          bool split = false;
+          for (const Launch &L : sched) split = split || L.r.nseg > 1 || (L.r.flags & (GF_SPLIT_OUT | GF_D_SPLIT));
+          if ((e = launch_persist(pa, split, sg)) != hipSuccess) return hip_fail(e, "Newton-Schulz launch (persistent)");
+          ++ns_launches;
+          continue;
+        }
         if (grp == PG_HEAD) {
           // one workgroup per block runs its whole iteration
           const TileDev *tl = reinterpret_cast<const TileDev *>(wsb + W.off_tiles[grp][TL_MN128]);

@@ -58,4 +58,19 @@ struct HeadArgs {
 hipError_t launch_head(const HeadArgs &a, int nprob, hipStream_t s);
 hipError_t launch_gemm256(const GemmArgs &a, int ntiles, hipStream_t s);
 
+// The persistent launch of a large-tile group: one workgroup per CU (8 XCDs
+// of 32), each walking the queue of its XCD.
+struct PersistArgs {
+  const ProbDev *probs;
+  char *ws;
+  const float *scales;
+  const int32_t *skip;         // may be NULL; non-zero: the launch does nothing
+  const PLaunch *launches;     // the group's schedule
+  const TileDev *items;        // the queues of XCD 0 .. 7, concatenated
+  const int32_t *ntl;          // [problem][2]: tiles of its m x m and m x n lists
+  int32_t *counters;           // PQ_PAD-strided dequeue and completion counters, zero
+  int32_t qoff[PQ_XCDS + 1];   // queue x = items[qoff[x], qoff[x + 1])
+};
+hipError_t launch_persist(const PersistArgs &a, bool split, hipStream_t s);
+
 }  // namespace muon

@@ -210,30 +210,23 @@ struct Src {
 
 // SPLIT: the recipe may carry K segments, a split D and a split output; the
 // plain instance keeps the single-segment pipeline free of them.
-template <bool SPLIT>
-__global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles) {
-  __shared__ __attribute__((aligned(1024))) char lds[2 * 2 * OPB];
-  if (args.skip && *args.skip) return;
+// LDS of both kernels: two stage buffers of both operands (the epilogue
+// stages through the first 67.5 KB), then a slot through which the
+// persistent kernel hands a work item to every wave.
+constexpr int LDS_SLOT = 2 * 2 * OPB;
+__shared__ __attribute__((aligned(1024))) char lds[LDS_SLOT + 64];
 
-#if MUON_XCD_REMAP
-  // Workgroup i runs on XCD i % 8.  The tile list is cut into chunks of
-  // 8 x 32 tiles; XCD x takes tiles [32 x, 32 x + 32) of each chunk, i.e.
-  // about two tile-rows of one problem, so the 32 CUs of an XCD share their
-  // operand panels through its L2 while all XCDs stay on the same problem.
-  const int xcd = (int)(blockIdx.x % NXCD), slot = (int)(blockIdx.x / NXCD);
-  const int t = (slot / XCD_CUS) * (NXCD * XCD_CUS) + xcd * XCD_CUS + slot % XCD_CUS;
-  if (t >= ntiles) return;
-#else
-  const int t = blockIdx.x;
-#endif
-  const TileDev tile = args.tiles[t];
-  const ProbDev &P = args.probs[tile.prob];
-  const GemmRecipe R = args.r;
+// One 256 x 256 output tile of recipe R: main loop and epilogue.  tid is
+// the thread's index in the workgroup.
+template <bool SPLIT>
+__device__ __forceinline__ void gemm_tile(const ProbDev *probs, char *ws, const float *scales, const GemmRecipe R,
+                                          const TileDev tile, const int tid) {
+  const ProbDev &P = probs[tile.prob];
   const int64_t M = R.dimM ? P.n : P.m;
   const int64_t N = R.dimN ? P.n : P.m;
   const int64_t K = R.dimK ? P.n : P.m;
-  const char *A = args.ws + P.off[R.rA];
-  const char *B = args.ws + P.off[R.rB];
+  const char *A = ws + P.off[R.rA];
+  const char *B = ws + P.off[R.rB];
   const int64_t lda = P.ld[R.rA], ldb = P.ld[R.rB];
   // K segments 1, 2 of a split product read (rA2[s-1], rB2[s-1]), which the
   // planner lays out with the leading dimensions of rA and rB
@@ -246,7 +239,6 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
   }
   const int64_t m0 = (int64_t)tile.tm * BT, n0 = (int64_t)tile.tn * BT;
 
-  const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int lr = lane & 31, lg = lane >> 5;
@@ -499,7 +491,7 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
   constexpr int SLD = 264;  // staging row stride (floats)
   float sc = 1.f;
   if (R.scale_pow) {
-    const float sv = args.scales[tile.prob];
+    const float sv = scales[tile.prob];
     sc = R.scale_pow == 2 ? sv * sv : sv;
   }
   const bool mirror = (R.flags & GF_SYM) && tile.tm != tile.tn;
@@ -507,14 +499,14 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
   const bool t1 = (R.flags & GF_S1_TRANS) != 0;
   const bool f0 = (R.flags & GF_S0_F32) != 0, f1 = (R.flags & GF_S1_F32) != 0, fd = (R.flags & GF_D_F32) != 0;
   const bool diag = (R.flags & GF_DIAG) != 0;
-  const char *D = R.rD >= 0 ? args.ws + P.off[R.rD] : nullptr;
+  const char *D = R.rD >= 0 ? ws + P.off[R.rD] : nullptr;
   const int64_t ldd = R.rD >= 0 ? P.ld[R.rD] : 0;
   const bool dsplit = SPLIT && (R.flags & GF_D_SPLIT) != 0;
-  const char *D2 = dsplit ? args.ws + P.off[R.rD2] : nullptr;
+  const char *D2 = dsplit ? ws + P.off[R.rD2] : nullptr;
   const bool osplit = SPLIT && (R.flags & GF_SPLIT_OUT) != 0;
-  char *S0 = args.ws + P.off[R.rS0];
+  char *S0 = ws + P.off[R.rS0];
   const int64_t ld0 = P.ld[R.rS0];
-  char *S1 = R.rS1 >= 0 ? args.ws + P.off[R.rS1] : nullptr;
+  char *S1 = R.rS1 >= 0 ? ws + P.off[R.rS1] : nullptr;
   const int64_t ld1 = R.rS1 >= 0 ? P.ld[R.rS1] : 0;
   const bool col_phase = t0 || (S1 && t1) || mirror;
   // Interior tile with bf16 operands and 16-byte aligned rows: the row phase
@@ -720,6 +712,77 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
   }
 }
 
+template <bool SPLIT>
+__global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles) {
+  if (args.skip && *args.skip) return;
+#if MUON_XCD_REMAP
+  // Workgroup i runs on XCD i % 8.  The tile list is cut into chunks of
+  // 8 x 32 tiles; XCD x takes tiles [32 x, 32 x + 32) of each chunk, i.e.
+  // about two tile-rows of one problem, so the 32 CUs of an XCD share their
+  // operand panels through its L2 while all XCDs stay on the same problem.
+  const int xcd = (int)(blockIdx.x % NXCD), slot = (int)(blockIdx.x / NXCD);
+  const int t = (slot / XCD_CUS) * (NXCD * XCD_CUS) + xcd * XCD_CUS + slot % XCD_CUS;
+  if (t >= ntiles) return;
+#else
+  const int t = blockIdx.x;
+#endif
+  gemm_tile<SPLIT>(args.probs, args.ws, args.scales, args.r, args.tiles[t], (int)threadIdx.x);
+}
+
+// Dependency waits poll about once a microsecond; past this many polls the
+// item runs anyway, so a fault in the queues shows as wrong results (which
+// the parity checks catch), never as a hang.
+constexpr int kMaxPolls = 1 << 22;
+
+// Persistent grouped launch: one workgroup per CU walks the work queue of
+// its XCD, named by the XCC_ID hardware register (bits 3:0), one tile of one
+// product of one problem per item.  Every product of a problem runs on the
+// XCD its problem was given, so producer and consumer tiles meet in that
+// XCD's L2: a finished tile is counted in done[problem] only after every
+// wave's stores have reached the L2, and a consumer invalidates its L1
+// before it reads.  A queue lists all tiles of a problem's product k before
+// any tile of its product k + 1, so an item waits only on items of smaller
+// index, which running workgroups hold: every dequeued item completes.
+template <bool SPLIT>
+__global__ __launch_bounds__(NTHR, 1) void ns_persist(PersistArgs pa) {
+  if (pa.skip && *pa.skip) return;
+  const int xcd = __builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) & (PQ_XCDS - 1);
+  int32_t *slot = reinterpret_cast<int32_t *>(lds + LDS_SLOT);
+  int32_t *head = pa.counters + PQ_PAD * xcd;
+  const int q0 = pa.qoff[xcd], qn = pa.qoff[xcd + 1] - q0;
+  if (threadIdx.x == 0) slot[0] = atomicAdd(head, 1);
+  __syncthreads();
+  int cur = __builtin_amdgcn_readfirstlane(slot[0]);
+  while (cur < qn) {
+    const TileDev it = pa.items[q0 + cur];
+    const int p = it.prob & PQ_PROB_MASK, k = (int)((uint32_t)it.prob >> PQ_LAUNCH_SHIFT);
+    const PLaunch &L = pa.launches[k];
+    int32_t *done = pa.counters + PQ_PAD * (PQ_XCDS + p);
+    int nxt = 0;
+    if (threadIdx.x == 0) {
+      nxt = atomicAdd(head, 1);  // the next item, taken now so its latency hides under this tile
+      const int need = L.mm_before * pa.ntl[2 * p] + L.mn_before * pa.ntl[2 * p + 1];
+      for (int n = 0; n < kMaxPolls && __hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need; ++n)
+        __builtin_amdgcn_s_sleep(2);
+    }
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    // the thread index is re-read for every item, so nothing derived from it
+    // is hoisted out of the loop and held in registers across the epilogue
+    int tid = (int)threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    gemm_tile<SPLIT>(pa.probs, pa.ws, pa.scales, L.r, TileDev{p, it.tm, it.tn}, tid);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      atomicAdd(done, 1);
+      slot[0] = nxt;
+    }
+    __syncthreads();
+    cur = __builtin_amdgcn_readfirstlane(slot[0]);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm256(const GemmArgs &a, int ntiles, hipStream_t s) {
@@ -733,6 +796,12 @@ hipError_t launch_gemm256(const GemmArgs &a, int ntiles, hipStream_t s) {
   const int grid = ntiles;
 #endif
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NTHR), 0, s, a, ntiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_persist(const PersistArgs &a, bool split, hipStream_t s) {
+  auto kern = split ? ns_persist<true> : ns_persist<false>;
+  hipLaunchKernelGGL(kern, dim3(PQ_XCDS * XCD_CUS), dim3(NTHR), 0, s, a);
   return hipGetLastError();
 }
 

@@ -136,6 +136,64 @@ static std::vector<Launch> build_split_gram_schedule(const muon_options &o, bool
   return S;
 }
 
+// Persistent schedule of a wave's large-tile groups.  The group's problems
+// go to the PQ_XCDS queues largest first, each to the queue with the least
+// work so far (the wave's problem order is already largest first); a queue
+// then lists, launch by launch of the group's schedule, every tile of each
+// of its problems in the order of the tile lists.  Every product of a
+// problem thus runs on one XCD, after all tiles of its previous product.
+static void build_queues(const muon_plan *p, WavePlan &W) {
+  const int np = (int)W.probs.size();
+  W.pntl.assign(2 * (size_t)np, 0);
+  for (int g = PG_BF16_BIG; g < NGROUPS; ++g) {
+    const std::vector<Launch> &S = p->schedule[g];
+    const std::vector<TileDev> &MM = W.tiles[g][TL_MM256], &MN = W.tiles[g][TL_MN256];
+    if (MN.empty() || S.empty() || S.size() > (size_t)PQ_MAX_LAUNCHES) continue;
+    bool gemm = true;
+    for (const Launch &L : S) gemm = gemm && L.kind == Launch::GEMM_OP;
+    if (!gemm) continue;
+    std::vector<int64_t> mm0(np, -1), mn0(np, -1);
+    for (size_t i = 0; i < MM.size(); ++i) {
+      if (mm0[MM[i].prob] < 0) mm0[MM[i].prob] = (int64_t)i;
+      ++W.pntl[2 * MM[i].prob];
+    }
+    for (size_t i = 0; i < MN.size(); ++i) {
+      if (mn0[MN[i].prob] < 0) mn0[MN[i].prob] = (int64_t)i;
+      ++W.pntl[2 * MN[i].prob + 1];
+    }
+    double load[PQ_XCDS] = {};
+    std::vector<int32_t> xp[PQ_XCDS];
+    for (int li = 0; li < np; ++li) {
+      if (mn0[li] < 0) continue;
+      int best = 0;
+      for (int x = 1; x < PQ_XCDS; ++x)
+        if (load[x] < load[best]) best = x;
+      load[best] += p->probs[W.problems[li]].flops;
+      xp[best].push_back(li);
+    }
+    std::vector<TileDev> &Q = W.pq[g];
+    Q.clear();
+    for (int x = 0; x < PQ_XCDS; ++x) {
+      W.pq_off[g][x] = (int32_t)Q.size();
+      for (size_t k = 0; k < S.size(); ++k)
+        for (int32_t li : xp[x]) {
+          const std::vector<TileDev> &L = S[k].mn ? MN : MM;
+          const int64_t a = S[k].mn ? mn0[li] : mm0[li];
+          const int32_t n = W.pntl[2 * li + (S[k].mn ? 1 : 0)];
+          for (int32_t i = 0; i < n; ++i)
+            Q.push_back(TileDev{li | (int32_t)(k << PQ_LAUNCH_SHIFT), L[a + i].tm, L[a + i].tn});
+        }
+    }
+    W.pq_off[g][PQ_XCDS] = (int32_t)Q.size();
+    W.pl[g].clear();
+    int32_t mmc = 0, mnc = 0;
+    for (const Launch &L : S) {
+      W.pl[g].push_back(PLaunch{L.r, mmc, mnc});
+      (L.mn ? mnc : mmc) += 1;
+    }
+  }
+}
+
 // Launch schedule of one operand class (bf16 = bf16 MFMA operands on the
 // m x n side; the Gram form's m x m chain is fp32 in both classes).
 static std::vector<Launch> build_schedule(const muon_options &o, bool bf16) {
@@ -466,6 +524,7 @@ muon_status build_plan(muon_plan *p) {
     }
     W.k1_tiles = k1t;
     max_k1 = std::max<int64_t>(max_k1, k1t);
+    if (o.schedule == MUON_SCHED_PERSISTENT) build_queues(p, W);
     int64_t ch = 0;
     for (int32_t i : W.matrices) {
       const MatrixPlan &M = p->mats[i];
@@ -487,6 +546,15 @@ muon_status build_plan(muon_plan *p) {
     for (int g = 0; g < NGROUPS; ++g)
       for (int l = 0; l < NLISTS; ++l) W.off_tiles[g][l] = tab.take((int64_t)W.tiles[g][l].size() * sizeof(TileDev));
     W.off_runs = tab.take((int64_t)W.runs.size() * sizeof(K3Run));
+    W.off_pntl = tab.take((int64_t)W.pntl.size() * 4);
+    for (int g = 0; g < NGROUPS; ++g) {
+      if (W.pq[g].empty()) continue;
+      W.off_pq[g] = tab.take((int64_t)W.pq[g].size() * sizeof(TileDev));
+      W.off_pl[g] = tab.take((int64_t)W.pl[g].size() * sizeof(PLaunch));
+      // the counters stay zero in the serialized tables, so every upload
+      // clears them
+      W.off_pcnt[g] = tab.take((int64_t)(PQ_XCDS + W.probs.size()) * PQ_PAD * 4);
+    }
   }
   // the accumulation and scatter tables reuse the head of the table region
   int64_t scatter_runs = 0;
@@ -526,6 +594,11 @@ muon_status build_plan(muon_plan *p) {
     for (int g = 0; g < NGROUPS; ++g)
       for (int l = 0; l < NLISTS; ++l) put(W.off_tiles[g][l], W.tiles[g][l]);
     put(W.off_runs, W.runs);
+    put(W.off_pntl, W.pntl);
+    for (int g = 0; g < NGROUPS; ++g) {
+      put(W.off_pq[g], W.pq[g]);
+      put(W.off_pl[g], W.pl[g]);
+    }
   }
   return MUON_OK;
 }
@@ -548,6 +621,7 @@ muon_status muon_default_options(muon_options *out) {
   out->precision = MUON_PREC_BF16;
   out->grad_dtype = MUON_DT_BF16;
   out->max_inflight_bytes = 0;
+  out->schedule = MUON_SCHED_LAUNCHES;
   return MUON_OK;
 }
 
@@ -568,6 +642,10 @@ muon_status muon_plan_create(muon_plan **out, const muon_matrix *mats, int32_t n
   if (opt->ns_steps < 0 || opt->ns_steps > 64) { set_error("ns_steps must be in [0, 64]"); return MUON_ERR_INVALID_ARG; }
   if (!(opt->beta >= 0.0f && opt->beta < 1.0f)) { set_error("beta must be in [0, 1)"); return MUON_ERR_INVALID_ARG; }
   if (opt->nesterov != 0 && opt->nesterov != 1) { set_error("nesterov must be 0 or 1"); return MUON_ERR_INVALID_ARG; }
+  if (opt->schedule != MUON_SCHED_LAUNCHES && opt->schedule != MUON_SCHED_PERSISTENT) {
+    set_error("unknown Newton-Schulz schedule"); return MUON_ERR_INVALID_ARG;
+  }
+  if (opt->reserved != 0) { set_error("options: reserved must be 0"); return MUON_ERR_INVALID_ARG; }
   if (!std::isfinite(opt->a) || !std::isfinite(opt->b) || !std::isfinite(opt->c) || !(opt->eps >= 0.0f) ||
       !std::isfinite(opt->eps)) {
     set_error("coefficients must be finite and eps >= 0"); return MUON_ERR_INVALID_ARG;

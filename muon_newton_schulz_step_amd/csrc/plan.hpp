@@ -57,6 +57,16 @@ struct WavePlan {
   int32_t k1_tiles = 0;
   int64_t k3_chunks = 0;
   int64_t k3_base = 0;   // index of this wave's first K3 chunk over all waves
+  // persistent schedule of the large-tile groups (empty unless the options
+  // ask for it): per group the queues of XCD 0..7 concatenated, their
+  // bounds, the schedule as the kernel reads it, and the byte offsets of
+  // these and of the group's counters in the workspace; per problem of the
+  // wave the tile counts of its two lists
+  std::vector<TileDev> pq[NGROUPS];
+  int32_t pq_off[NGROUPS][PQ_XCDS + 1] = {};
+  std::vector<PLaunch> pl[NGROUPS];
+  std::vector<int32_t> pntl;
+  int64_t off_pq[NGROUPS] = {}, off_pl[NGROUPS] = {}, off_pcnt[NGROUPS] = {}, off_pntl = 0;
 };
 
 // Address range of one buffer of a call, for the overlap check.

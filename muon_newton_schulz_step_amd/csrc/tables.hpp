@@ -155,4 +155,26 @@ constexpr int32_t GF_DIAG = 128;     // add cdiag on the diagonal
 constexpr int32_t GF_SPLIT_OUT = 256;  // S0 = bf16(v), S1 = bf16(v - S0): a hi/lo pair
 constexpr int32_t GF_D_SPLIT = 512;    // D = bf16 hi (rD) + bf16 lo (rD2)
 
+// Persistent schedule of a large-tile group (one launch for every product of
+// every problem): a queue of work items per XCD.  An item is a TileDev whose
+// prob field holds the problem (wave-local index) in its low 24 bits and the
+// launch of the group's schedule in its high 8 bits.
+constexpr int PQ_XCDS = 8;
+constexpr int32_t PQ_PROB_MASK = 0xFFFFFF;
+constexpr int PQ_LAUNCH_SHIFT = 24;
+constexpr int PQ_MAX_LAUNCHES = 255;
+// Counters, one per 128-byte line so that no two XCDs ever touch one line:
+// counters[PQ_PAD x] is XCD x's dequeue position, counters[PQ_PAD (PQ_XCDS + p)]
+// the finished tiles of problem p.  Zero when the launch starts.
+constexpr int PQ_PAD = 32;
+
+// One launch of the schedule as the persistent kernel reads it: the recipe
+// and how many launches over each tile list precede it, so that product k
+// of problem p may start once p has finished
+//   mm_before * (tiles of its m x m list) + mn_before * (tiles of its m x n list).
+struct PLaunch {
+  GemmRecipe r;
+  int32_t mm_before, mn_before;
+};
+
 }  // namespace muon

@@ -14,12 +14,18 @@
 //     with m >= 256; the blocks fused into one workgroup each are exactly
 //     the bf16 blocks with 64 <= m <= 128 (at least one step), listed once,
 //     with no m x m buffer, no tile elsewhere and U apart from what they read;
+//   - the persistent queues hold exactly the tiles of every launch of the
+//     large-tile schedules, each problem in one queue with its launches in
+//     order, with the counts the kernel's dependency test reads and zero
+//     counters, spread over the queues as LPT spreads them;
 //   - every K1 entry covers its block, every owned run lies inside its
 //     matrix and its partition, the chunk prefixes count the chunks exactly;
 //   - the serialized tables fit their region and the scratch sums follow it.
 // Invalid groups are refused with the documented status.  Exit status 0 and
 // the line "plan invariants ok" mean every check held.
 #include <algorithm>
+#include <array>
+#include <cstring>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -35,6 +41,7 @@ using namespace muon;
 namespace {
 
 int g_fail = 0;
+uint64_t g_queued = 0;  // plans with at least one persistent queue
 
 void fail(const std::string &what, uint64_t it) {
   if (g_fail < 20) std::fprintf(stderr, "iteration %llu: %s\n", (unsigned long long)it, what.c_str());
@@ -187,6 +194,74 @@ void check_plan(const muon_plan *p, uint64_t it) {
         }
       }
     }
+    // persistent queues: for every large-tile group, exactly the tiles of
+    // every launch of its schedule, each problem's items in one queue with
+    // its launches in order (an item then waits only on earlier items of
+    // its own queue), the tile counts and launch prefixes the kernel's
+    // dependency test reads, zero counters, and an LPT spread of the work
+    {
+      const int np = (int)W.probs.size();
+      const bool persistent = p->opt.schedule == MUON_SCHED_PERSISTENT;
+      for (int g = 0; g < NGROUPS; ++g) {
+        const std::vector<TileDev> &Q = W.pq[g];
+        const std::vector<Launch> &S = p->schedule[g];
+        const std::vector<TileDev> &MM = W.tiles[g][TL_MM256], &MN = W.tiles[g][TL_MN256];
+        const bool want = persistent && g >= PG_BF16_BIG && !MN.empty() && p->opt.ns_steps > 0;
+        if (want != !Q.empty()) { fail("persistent queue presence", it); continue; }
+        if (Q.empty()) continue;
+        ++g_queued;
+        if (W.pq_off[g][0] != 0 || W.pq_off[g][PQ_XCDS] != (int32_t)Q.size()) fail("queue bounds", it);
+        for (int x = 0; x < PQ_XCDS; ++x)
+          if (W.pq_off[g][x] > W.pq_off[g][x + 1]) fail("queue bounds out of order", it);
+        if (!in_tables(W.off_pq[g], (int64_t)(Q.size() * sizeof(TileDev))) ||
+            !in_tables(W.off_pl[g], (int64_t)(W.pl[g].size() * sizeof(PLaunch))) ||
+            !in_tables(W.off_pcnt[g], (int64_t)(PQ_XCDS + np) * PQ_PAD * 4) ||
+            !in_tables(W.off_pntl, (int64_t)W.pntl.size() * 4))
+          fail("a persistent table leaves the table region", it);
+        for (int64_t b = 0; b < (int64_t)(PQ_XCDS + np) * PQ_PAD * 4; ++b)
+          if (p->host_tables[W.off_pcnt[g] + b] != 0) { fail("persistent counters not zero", it); break; }
+        // the items against the schedule's launches over the tile lists
+        std::vector<std::array<int32_t, 4>> want_items, got_items;
+        for (size_t k = 0; k < S.size(); ++k)
+          for (const TileDev &t : (S[k].mn ? MN : MM)) want_items.push_back({t.prob, (int32_t)k, t.tm, t.tn});
+        std::vector<int> xcd_of(np, -1), last_k(np, -1);
+        std::vector<double> load(PQ_XCDS, 0.0);
+        double biggest = 0.0;
+        for (int x = 0; x < PQ_XCDS; ++x)
+          for (int32_t i = W.pq_off[g][x]; i < W.pq_off[g][x + 1]; ++i) {
+            const int32_t pr = Q[i].prob & PQ_PROB_MASK, k = (int32_t)((uint32_t)Q[i].prob >> PQ_LAUNCH_SHIFT);
+            got_items.push_back({pr, k, Q[i].tm, Q[i].tn});
+            if (pr < 0 || pr >= np || k >= (int32_t)S.size()) { fail("queue item out of range", it); continue; }
+            if (xcd_of[pr] < 0) {
+              xcd_of[pr] = x;
+              const double f = p->probs[W.problems[pr]].flops;
+              load[x] += f;
+              biggest = std::max(biggest, f);
+            }
+            if (xcd_of[pr] != x) fail("a problem in two queues", it);
+            if (k < last_k[pr]) fail("a problem's launches out of order in its queue", it);
+            last_k[pr] = k;
+          }
+        std::sort(want_items.begin(), want_items.end());
+        std::sort(got_items.begin(), got_items.end());
+        if (want_items != got_items) fail("queue items differ from the schedule's tiles", it);
+        const auto mm = std::minmax_element(load.begin(), load.end());
+        if (*mm.second - *mm.first > biggest * (1 + 1e-9)) fail("queues not balanced as LPT", it);
+        // tile counts per problem and the launch prefixes
+        std::vector<int32_t> nmm(np, 0), nmn(np, 0);
+        for (const TileDev &t : MM) ++nmm[t.prob];
+        for (const TileDev &t : MN) ++nmn[t.prob];
+        for (int pr = 0; pr < np; ++pr)
+          if (nmn[pr] && (W.pntl[2 * pr] != nmm[pr] || W.pntl[2 * pr + 1] != nmn[pr])) fail("problem tile counts", it);
+        if (W.pl[g].size() != S.size()) { fail("launch table size", it); continue; }
+        int32_t cm = 0, cn = 0;
+        for (size_t k = 0; k < S.size(); ++k) {
+          if (W.pl[g][k].mm_before != cm || W.pl[g][k].mn_before != cn) fail("launch prefixes", it);
+          if (std::memcmp(&W.pl[g][k].r, &S[k].r, sizeof(GemmRecipe)) != 0) fail("launch recipe", it);
+          (S[k].mn ? cn : cm) += 1;
+        }
+      }
+    }
     // K1 entries
     int32_t k1t = 0;
     for (const K1Prob &k : W.k1) {
@@ -260,6 +335,7 @@ int main(int argc, char **argv) {
     o.precision = (rng() % 4) ? MUON_PREC_BF16 : MUON_PREC_FP32;
     o.ns_steps = (int)(rng() % 6);
     o.grad_dtype = (rng() & 1) ? MUON_DT_BF16 : MUON_DT_FP32;
+    o.schedule = (rng() & 1) ? MUON_SCHED_PERSISTENT : MUON_SCHED_LAUNCHES;
     const int R = 1 + (int)(rng() % 5);
     muon_layout lay;
     lay.num_partitions = R;
@@ -308,6 +384,7 @@ int main(int argc, char **argv) {
     std::fprintf(stderr, "%d failures\n", g_fail);
     return 1;
   }
-  std::printf("plan invariants ok: %llu plans\n", (unsigned long long)planned);
+  std::printf("plan invariants ok: %llu plans, %llu persistent queues\n", (unsigned long long)planned,
+              (unsigned long long)g_queued);
   return 0;
 }

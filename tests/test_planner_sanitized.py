@@ -38,3 +38,6 @@ def test_planner_invariants_under_sanitizers(checker, seed):
     r = subprocess.run([checker, str(seed), "150"], capture_output=True, text=True, env=env, timeout=600)
     assert r.returncode == 0, (r.stdout + r.stderr)[-4000:]
     assert "plan invariants ok" in r.stdout
+    # the random groups include large-tile blocks under the persistent schedule
+    queued = int(r.stdout.split("plans, ")[1].split()[0])
+    assert queued > 0, r.stdout
