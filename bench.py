@@ -207,8 +207,9 @@ def main() -> int:
     ap.add_argument("--gram-steps", type=int, default=2,
                     help="timed steps of a second leg in the Gram form when the workload runs both forms and the "
                          "headline is the standard one (0: no Gram leg)")
-    ap.add_argument("--max-inflight-gb", type=float, default=0.0,
-                    help="cap the Newton-Schulz workspace at this many GB (the group then runs in waves)")
+    ap.add_argument("--max-inflight-gb", type=float, default=None,
+                    help="cap the Newton-Schulz workspace at this many GB (the group then runs in waves; default: "
+                         "the library's default cap, 24 GiB; 0: no cap)")
     ap.add_argument("--schedule", default="launches", choices=["launches", "persistent"],
                     help="Newton-Schulz schedule of the large-tile blocks: one launch per product, or one "
                          "persistent launch per wave with per-block dependency counters")
@@ -243,7 +244,7 @@ def main() -> int:
     method = args.method or wl.methods[0]
     offsets, P = M.pack_layout(wl.shapes, wl.num_partitions, wl.align)
     step_dtype = "fp32" if wl.gas > 1 else wl.micro_dtype
-    cap = int(args.max_inflight_gb * 1e9)
+    cap = None if args.max_inflight_gb is None else int(args.max_inflight_gb * 1e9)
 
     def make_group(meth):
         return M.MuonGroup(wl.shapes, heads=wl.heads, offsets=offsets, num_partitions=wl.num_partitions,

@@ -119,7 +119,7 @@ typedef struct {
   float eps;           /* X <- u / (||u||_F + eps), per block              */
   int32_t precision;   /* muon_ns_precision                                */
   int32_t grad_dtype;  /* muon_dtype of the grads given to muon_step       */
-  uint64_t max_inflight_bytes; /* cap on the workspace; 0 = no cap          */
+  uint64_t max_inflight_bytes; /* cap on the workspace's data; 0 = no cap  */
   int32_t schedule;    /* muon_ns_schedule                                 */
   int32_t reserved;    /* must be 0                                        */
 } muon_options;
@@ -167,11 +167,17 @@ typedef struct {
   double flops;       /* nominal Newton-Schulz flops of this problem */
 } muon_problem_info;
 
+/* The default workspace cap: groups needing more run in waves (measured on
+ * MI355X: no slower for the Llama-7B and per-head groups, faster for the
+ * 70B share, against one wave). */
+#define MUON_DEFAULT_INFLIGHT_BYTES ((uint64_t)24 << 30)
+
 typedef struct muon_plan muon_plan;
 
 /* Default options: beta 0.95, Nesterov on, standard form, 5 steps,
  * (a,b,c) = (3.4445, -4.7750, 2.0315), eps 1e-7, bf16 precision, bf16
- * grads, no workspace cap, one launch per product.  Errors: INVALID_ARG if out is NULL. */
+ * grads, the workspace's data capped at MUON_DEFAULT_INFLIGHT_BYTES (24 GiB:
+ * a larger group runs in waves), one launch per product.  Errors: INVALID_ARG if out is NULL. */
 muon_status muon_default_options(muon_options *out);
 
 /* Build a plan for a group of n matrices (host only; no device call).
@@ -188,7 +194,8 @@ muon_status muon_plan_create(muon_plan **out, const muon_matrix *mats, int32_t n
  * caller allocates it: the library holds no device memory of its own, in
  * place of the gather-buffer cache ([8464] "Changes": cached gather buffers
  * capped at 256 MB and freed on destroy).  With opt.max_inflight_bytes set
- * it is proportional to the matrices in flight, not to the whole group
+ * (as by default) it is proportional to the matrices in flight, not to the
+ * whole group
  * ([8526] description: temporary memory proportional to the largest Muon
  * group).  Errors: INVALID_ARG for NULL. */
 muon_status muon_plan_workspace_bytes(const muon_plan *p, size_t *bytes);

@@ -69,7 +69,7 @@ class MuonGroup:
     def __init__(self, shapes, heads=None, offsets=None, num_partitions: int = 1, partition_numel=None,
                  align: int = 16, method: str = "standard", precision: str = "bf16", grad_dtype: str = "bf16",
                  ns_steps: int = 5, beta: float = 0.95, nesterov: bool = True, coeffs=None, eps=None,
-                 max_inflight_bytes: int = 0, schedule: str = "launches"):
+                 max_inflight_bytes=None, schedule: str = "launches"):
         self.shapes = [(int(r), int(c)) for r, c in shapes]
         self.heads = list(heads) if heads is not None else [0] * len(self.shapes)
         if offsets is None or partition_numel is None:
@@ -93,7 +93,8 @@ class MuonGroup:
             o.eps = eps
         o.precision = PRECISION[precision]
         o.grad_dtype = DTYPE[grad_dtype]
-        o.max_inflight_bytes = int(max_inflight_bytes)
+        if max_inflight_bytes is not None:  # None: the library's default cap; 0: no cap
+            o.max_inflight_bytes = int(max_inflight_bytes)
         o.schedule = SCHEDULE[schedule]
         self.options = o
         lay = muon_layout(self.partition_numel, self.num_partitions, 0)

@@ -620,7 +620,7 @@ muon_status muon_default_options(muon_options *out) {
   out->eps = 1e-7f;
   out->precision = MUON_PREC_BF16;
   out->grad_dtype = MUON_DT_BF16;
-  out->max_inflight_bytes = 0;
+  out->max_inflight_bytes = MUON_DEFAULT_INFLIGHT_BYTES;
   out->schedule = MUON_SCHED_LAUNCHES;
   return MUON_OK;
 }

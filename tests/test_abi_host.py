@@ -41,6 +41,7 @@ def test_default_options():
     assert o.beta == pytest.approx(0.95) and o.nesterov == 1 and o.ns_steps == 5
     assert (o.a, o.b, o.c) == pytest.approx((3.4445, -4.7750, 2.0315))
     assert o.method == 0 and o.precision == 1
+    assert o.max_inflight_bytes == 24 << 30 and o.schedule == 0 and o.reserved == 0
 
 
 def _group(shapes, **kw):
