@@ -99,7 +99,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ns_gemm_llama7b_32layer_hbm_traff
 # the sources behind the Llama-7B group's Newton-Schulz launches (all of its
 # blocks are 4096 wide, so they run on the large-tile kernel only)
 TRAFFIC_SOURCES = ("muon_newton_schulz_step_amd/csrc/k_gemm256.hip", "muon_newton_schulz_step_amd/csrc/plan.cpp",
-                   "muon_newton_schulz_step_amd/csrc/tables.hpp")
+                   "muon_newton_schulz_step_amd/csrc/tables.hpp", "include/muon.h")
 
 
 def traffic_sources_hash() -> str:
@@ -118,11 +118,10 @@ def traffic_sources_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, waves: int):
     """HBM bytes per Newton-Schulz launch from the committed FETCH_SIZE /
-    WRITE_SIZE summary, or None if it was taken on another workload or the
-    kernel sources changed since."""
-    import hashlib
+    WRITE_SIZE summary, or None if it was taken on another workload or wave
+    count (a launch covers one wave), or the kernel sources changed since."""
     if workload != "llama7b_32layer" or not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
@@ -130,7 +129,7 @@ def measured_traffic(workload: str):
         if ":" in ln and not ln.startswith(("|", "#", "`")):
             k, _, v = ln.partition(":")
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_src_sha256_16") != traffic_sources_hash():
+    if kv.get("kernel_src_sha256_16") != traffic_sources_hash() or kv.get("waves") != str(waves):
         return None
     try:
         return float(kv["ns_gemm_traffic_bytes_per_launch"])
@@ -397,7 +396,7 @@ def main() -> int:
         "apply_gbs": round(numel * 12 / (statistics.mean(apply_ms) * 1e-3) / 1e9, 1),
         "roofline": {"kernel": "ns_gemm (grouped Newton-Schulz GEMM)", "bound": "mfma",
                      "achieved": round(ns_tflops_sym, 1), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(ns_tflops_sym / peak, 4), "traffic": measured_traffic(wl.name),
+                     "frac": round(ns_tflops_sym / peak, 4), "traffic": measured_traffic(wl.name, waves),
                      "traffic_unit": "bytes per launch (HBM read + write, rocprofv3 FETCH_SIZE/WRITE_SIZE)",
                      "flops_per_step": sym, "launches_per_step": nl,
                      "avg_launch_ms": round(ns_ms / max(nl, 1), 4)},
