@@ -729,9 +729,10 @@ __global__ __launch_bounds__(NTHR, 1) void ns_gemm256(GemmArgs args, int ntiles)
   gemm_tile<SPLIT>(args.probs, args.ws, args.scales, args.r, args.tiles[t], (int)threadIdx.x);
 }
 
-// Dependency waits poll about once a microsecond; past this many polls the
-// item runs anyway, so a fault in the queues shows as wrong results (which
-// the parity checks catch), never as a hang.
+// Dependency waits poll about once a microsecond; past this many polls
+// (about four seconds) the item runs anyway and the workgroup stops waiting
+// for the rest of the launch, so a fault in the queues shows as wrong
+// results (which the parity checks catch) within seconds, never as a hang.
 constexpr int kMaxPolls = 1 << 22;
 
 // Persistent grouped launch: one workgroup per CU walks the work queue of
@@ -753,6 +754,7 @@ __global__ __launch_bounds__(NTHR, 1) void ns_persist(PersistArgs pa) {
   if (threadIdx.x == 0) slot[0] = atomicAdd(head, 1);
   __syncthreads();
   int cur = __builtin_amdgcn_readfirstlane(slot[0]);
+  int polls_left = kMaxPolls;  // thread 0's wait budget for the whole launch
   while (cur < qn) {
     const TileDev it = pa.items[q0 + cur];
     const int p = it.prob & PQ_PROB_MASK, k = (int)((uint32_t)it.prob >> PQ_LAUNCH_SHIFT);
@@ -762,8 +764,10 @@ __global__ __launch_bounds__(NTHR, 1) void ns_persist(PersistArgs pa) {
     if (threadIdx.x == 0) {
       nxt = atomicAdd(head, 1);  // the next item, taken now so its latency hides under this tile
       const int need = L.mm_before * pa.ntl[2 * p] + L.mn_before * pa.ntl[2 * p + 1];
-      for (int n = 0; n < kMaxPolls && __hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need; ++n)
+      while (polls_left > 0 && __hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
         __builtin_amdgcn_s_sleep(2);
+        --polls_left;
+      }
     }
     __syncthreads();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
