@@ -9,8 +9,8 @@
 //    operands from LDS for 16 MFMAs, half the LDS traffic per flop of a
 //    64 x 64 wave tile.
 //  - K staged 64 deep (128-byte rows) straight from global memory into LDS
-//    with 16-byte LDS-DMA loads (global_load_lds_dwordx4: lane L lands at
-//    base + 16 L), double buffered: the loads of stage t+1 are in flight
+//    with 16-byte LDS-DMA loads (buffer_load_dwordx4 ... lds: lane L lands
+//    at base + 16 L), double buffered: the loads of stage t+1 are in flight
 //    while stage t feeds the MFMAs.  The 16 DMA instructions of a stage are
 //    issued one per MFMA pair across two k-steps; issued back to back they
 //    stall the wave (and its MFMAs) until the address unit drains them,
@@ -264,6 +264,22 @@ __device__ __forceinline__ void gemm_tile(const ProbDev *probs, char *ws, const 
     brow[j] = min(n0 + r, N - 1) * ldb;
     lchunk[j] = swz(r, lpos) * 8;
   }
+  // Whole stages load as buffer loads into LDS: a descriptor per operand
+  // panel (scalar registers, based at the tile's first row and the stage's K
+  // offset) and a 32-bit byte offset per lane, instead of a 64-bit address
+  // per lane and instruction.
+  auto uni = [](const char *ptr) {
+    const uint64_t v = reinterpret_cast<uint64_t>(ptr);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const char *>(((uint64_t)hi << 32) | lo);
+  };
+  uint32_t aoff[8], boff[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    aoff[j] = (uint32_t)((arow[j] - m0 * lda + lchunk[j]) * 2);
+    boff[j] = (uint32_t)((brow[j] - n0 * ldb + lchunk[j]) * 2);
+  }
   const int nfull = (int)(K / KS);
   const int nk = (int)((K + KS - 1) / KS);
   const int nkt = SPLIT ? nk * R.nseg : nk;          // stages over all K segments
@@ -365,15 +381,20 @@ __device__ __forceinline__ void gemm_tile(const ProbDev *probs, char *ws, const 
       }
       return r;
     };
+    // descriptor word 3 of a raw dword buffer on gfx9 (32-bit data format)
+    constexpr int kRsrcWord3 = 0x00020000;
     auto dma1 = [&](const Src &sr, int st, int q) {
       char *la = lds + st * 2 * OPB + wv * 64 * ROWB;
       const int j = q & 7;
-      if (q < 8)
-        __builtin_amdgcn_global_load_lds(sr.a + (arow[j] + sr.k0 + lchunk[j]) * 2, (lds_void *)(la + j * 8 * ROWB),
-                                         16, 0, 0);
-      else
-        __builtin_amdgcn_global_load_lds(sr.b + (brow[j] + sr.k0 + lchunk[j]) * 2,
-                                         (lds_void *)(la + OPB + j * 8 * ROWB), 16, 0, 0);
+      if (q < 8) {
+        const auto rs = __builtin_amdgcn_make_buffer_rsrc((void *)uni(sr.a + (m0 * lda + sr.k0) * 2), (short)0,
+                                                          0x7fffffff, kRsrcWord3);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(la + j * 8 * ROWB), 16, aoff[j], 0, 0, 0);
+      } else {
+        const auto rs = __builtin_amdgcn_make_buffer_rsrc((void *)uni(sr.b + (n0 * ldb + sr.k0) * 2), (short)0,
+                                                          0x7fffffff, kRsrcWord3);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(la + OPB + j * 8 * ROWB), 16, boff[j], 0, 0, 0);
+      }
     };
     // fragment read q of a k-step, in the order the next step's MFMA pairs
     // consume them: A0, B0, B1, B2, B3, A1, A2, A3
