@@ -4,21 +4,24 @@
 // tile list, both operands row-major with K contiguous), for problems whose
 // small side is at least 256:
 //  - 256 x 256 output tile per workgroup of 4 wave64s (2 x 2), each wave
-//    128 x 128 = 4 x 4 blocks of v_mfma_f32_32x32x16_bf16, 256 fp32
-//    accumulators per lane.  Per 16-deep K step a wave reads 8 KB of
-//    operands from LDS for 16 MFMAs, half the LDS traffic per flop of a
-//    64 x 64 wave tile.
+//    128 x 128 = 8 x 8 blocks of v_mfma_f32_16x16x32_bf16, 256 fp32
+//    accumulators per lane.  Per 32-deep K step a wave reads 16 KB of
+//    operands from LDS for 64 MFMAs.  The 16 x 16 x 32 form issues the same
+//    flops as 32 x 32 x 16 in half-length instructions and, measured on this
+//    kernel, runs the whole step 5% faster (the register-only issue rate of
+//    the two differs by 11%, partly through the clock the chip holds); its
+//    accumulation order gives bitwise the same results here.
 //  - K staged 64 deep (128-byte rows) straight from global memory into LDS
 //    with 16-byte LDS-DMA loads (buffer_load_dwordx4 ... lds: lane L lands
-//    at base + 16 L), double buffered: the loads of stage t+1 are in flight
-//    while stage t feeds the MFMAs.  The 16 DMA instructions of a stage are
-//    issued one per MFMA pair across two k-steps; issued back to back they
-//    stall the wave (and its MFMAs) until the address unit drains them,
-//    which cost a third of the main loop.  A ragged last stage (K not a
-//    multiple of 64) goes through registers so elements at k >= K are
-//    zeroed.
+//    at base + 16 L), double buffered.  A stage is two k-steps; the barrier
+//    sits between them, and the 16 DMA instructions of stage t+2 go into
+//    the buffer it frees, one per group of four MFMAs of the second k-step.
+//    Issued back to back they stall the wave (and its MFMAs) until the
+//    address unit drains them.  A ragged last stage (K not a multiple of
+//    64) goes through registers so elements at k >= K are zeroed.
 //  - 16-byte chunks of each row are XOR-swizzled (position = chunk ^ f(row))
-//    so the 32 rows a fragment read touches spread over all LDS banks.
+//    so the 16 rows each quarter of a fragment read touches spread over all
+//    LDS banks.
 //  - Workgroup i runs on XCD i mod 8; the tile list (ordered in 4 x 8
 //    blocks per problem) is cut into chunks of 256 and XCD x takes entries
 //    [32 x, 32 x + 32) of each chunk, so the 32 CUs of an XCD work on one
@@ -48,6 +51,7 @@ namespace muon {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 namespace {
 
@@ -67,6 +71,14 @@ __device__ __forceinline__ int swz(int r, int c) {
 #else
   return c ^ ((r >> 1) & 7);
 #endif
+}
+
+// c += a b on v_mfma_f32_16x16x32_bf16 with the accumulator tied in place
+// (the compiler's own selection of this instruction picks a destination
+// apart from the accumulator and rotates 64 blocks every loop trip).
+// Results are read only after mfma_drain().
+__device__ __forceinline__ void mfma16(f32x4_t &c, const bf16x8_t &a, const bf16x8_t &b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
@@ -241,18 +253,18 @@ __device__ __forceinline__ void gemm_tile(const ProbDev *probs, char *ws, const 
 
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int lr = lane & 31, lg = lane >> 5;
+  const int lr = lane & 15, lg = lane >> 4;
 
   // loader geometry: wave w stages rows [64 w, 64 w + 64) of both operands,
   // 8 rows (1 KB) per instruction; lane L covers row 64w + 8j + L/8, LDS
   // chunk position L%8, which holds global chunk swz(row, L%8).
-  f32x16_t acc[4][4];
+  f32x4_t acc[8][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+      for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.f;
 
   const int lrow = lane >> 3, lpos = lane & 7;
   int64_t arow[8], brow[8];
@@ -319,58 +331,58 @@ __device__ __forceinline__ void gemm_tile(const ProbDev *probs, char *ws, const 
     }
   };
 
-  // fragment row offsets (bytes) and the per-row swizzle key
-  int arb[4], brb[4], ak[4], bk[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int ra_ = wm * 128 + i * 32 + lr, rb_ = wn * 128 + i * 32 + lr;
-    arb[i] = ra_ * ROWB; ak[i] = ra_;
-    brb[i] = rb_ * ROWB; bk[i] = rb_;
-  }
-  // Software pipeline over 16-deep k-steps: the fragments of step s+1 are
-  // read from LDS while the 16 MFMAs of step s run (two fragment sets).
-  // The stage barrier sits before the last k-step of each stage, so the
-  // first reads of the next stage overlap that step's MFMAs, and the
-  // LDS-DMA of stage t+2 is issued as soon as stage t's buffer is free.
-  bf16x8_t fa[2][4], fb[2][4];
-  auto read_frags = [&](int set, int st, int ks) {
+  // Fragments of v_mfma_f32_16x16x32_bf16 over a 32-deep k-step: lane L of
+  // block i holds row 16 i + L%16 of the wave's 128 rows, K elements
+  // 8 (L/16) .. +8 of the step, i.e. 16-byte chunk 4 ks + L/16 of the staged
+  // row.  Block rows are 16 apart, so a lane's swizzle key is the same for
+  // all eight blocks, and the second step's chunks are the first step's with
+  // bit 2 flipped: one LDS address per lane and operand, the block and step
+  // folded into immediate offsets.
+  const int pos0 = swz(lr, lg) * 16;
+  const int abase = (wm * 128 + lr) * ROWB + pos0;
+  const int bbase = (wn * 128 + lr) * ROWB + pos0;
+  bf16x8_t fa[2][8], fb[2][8];
+  auto rdA = [&](int set, int st, int ks, int i) {
     const char *la = lds + st * 2 * OPB;
-    const char *lb = la + OPB;
-    const int c = ks * 2 + lg;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fa[set][i] = *reinterpret_cast<const bf16x8_t *>(la + arb[i] + swz(ak[i], c) * 16);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) fb[set][j] = *reinterpret_cast<const bf16x8_t *>(lb + brb[j] + swz(bk[j], c) * 16);
+    fa[set][i] = *reinterpret_cast<const bf16x8_t *>(la + ((abase + i * 16 * ROWB) ^ (ks * 64)));
   };
-  auto mfmas = [&](int set) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
+  auto rdB = [&](int set, int st, int ks, int j) {
+    const char *lb = lds + st * 2 * OPB + OPB;
+    fb[set][j] = *reinterpret_cast<const bf16x8_t *>(lb + ((bbase + j * 16 * ROWB) ^ (ks * 64)));
   };
-  auto interleave = [&]() {
-    // 16 MFMAs with the 8 fragment reads of the next step between them
+  auto read_frags = [&](int set, int st, int ks) {
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int i = 0; i < 8; ++i) rdA(set, st, ks, i);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rdB(set, st, ks, j);
+  };
+  // read q of a k-step in the order the MFMAs consume them: A0, B0..B7, A1..A7
+  auto read1 = [&](int set, int st, int ks, int q) {
+    if (q == 0) rdA(set, st, ks, 0);
+    else if (q <= 8) rdB(set, st, ks, q - 1);
+    else rdA(set, st, ks, q - 8);
+  };
+  // One 32-deep k-step on fragment set `set`: 16 groups of four MFMAs (one
+  // block row, four block columns), the 16 fragment reads of the next step
+  // (stage buffer rst, k-step rks) in groups 0..11, two in each of groups
+  // 0..3, so they land four groups before the next step needs them, and
+  // dma(n) after group n.  sched_barrier keeps the groups in this order.
+  auto kstep = [&](int set, int rst, int rks, auto &&dma) {
+#pragma unroll
+    for (int n = 0; n < 16; ++n) {
+      const int i = n >> 1, j = (n & 1) * 4;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) mfma16(acc[i][j + jj], fa[set][i], fb[set][j + jj]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (n < 4) { read1(set ^ 1, rst, rks, 2 * n); read1(set ^ 1, rst, rks, 2 * n + 1); }
+      else if (n < 12) read1(set ^ 1, rst, rks, n + 4);
+      dma(n);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
+  auto no_dma = [](int) {};
   if (nfull == nk) {
-    // K a multiple of 64: every stage is a whole LDS-DMA stage.  The 16
-    // DMA instructions of stage t+2 are spread over two k-steps (one per
-    // MFMA pair): the A rows over the k-step after the barrier that frees
-    // the buffer, the B rows over the first k-step of the next stage.  A
-    // burst of 16 would hold up the wave's MFMAs until the address unit
-    // drains it.  The destination rows of this wave are uniform, so M0 is
-    // computed on the scalar unit.
     const int wv = __builtin_amdgcn_readfirstlane(wave);
-    // Source of stage kt of the concatenated K range: the segment's operand
-    // bases and the K offset inside the segment.  Chosen once per stage with
-    // selects, outside the MFMA groups: chosen per DMA instruction, the
-    // choice compiled to branches that split every MFMA pair into its own
-    // basic block.
     auto src_of = [&](int kt) {
       Src r{A, B, (int64_t)kt * KS};
       if (SPLIT) {
@@ -396,42 +408,6 @@ __device__ __forceinline__ void gemm_tile(const ProbDev *probs, char *ws, const 
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(la + OPB + j * 8 * ROWB), 16, boff[j], 0, 0, 0);
       }
     };
-    // fragment read q of a k-step, in the order the next step's MFMA pairs
-    // consume them: A0, B0, B1, B2, B3, A1, A2, A3
-    auto read1 = [&](int set, int st, int ks, int q) {
-      const char *la = lds + st * 2 * OPB;
-      const char *lb = la + OPB;
-      const int c = ks * 2 + lg;
-      if (q == 0) fa[set][0] = *reinterpret_cast<const bf16x8_t *>(la + arb[0] + swz(ak[0], c) * 16);
-      else if (q <= 4) fb[set][q - 1] = *reinterpret_cast<const bf16x8_t *>(lb + brb[q - 1] + swz(bk[q - 1], c) * 16);
-      else fa[set][q - 4] = *reinterpret_cast<const bf16x8_t *>(la + arb[q - 4] + swz(ak[q - 4], c) * 16);
-    };
-    // one 16-deep k-step on fragment set `set`, in eight groups of an MFMA
-    // pair, the fragment reads of the next step (RD: two in each of the first
-    // two groups, one in each of the next four) and one DMA instruction per
-    // group (DMA: instructions q0 .. q0 + 7 of the stage at dsrc into buffer
-    // dst); sched_barrier keeps the groups in this order
-    auto kstep = [&](int set, auto rd_, int rst, int rks, auto dma_, const Src &dsrc, int dst, int q0) {
-      constexpr bool RD = decltype(rd_)::value;
-      constexpr bool DMA = decltype(dma_)::value;
-#pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        const int i = n >> 1, j = (n & 1) * 2;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
-        acc[i][j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j + 1], acc[i][j + 1], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (RD) {
-          // the fragment reads of the next step finish two MFMA pairs
-          // before it starts (the wait there covers every outstanding read)
-          if (n < 2) { read1(set ^ 1, rst, rks, 2 * n); read1(set ^ 1, rst, rks, 2 * n + 1); }
-          else if (n < 6) read1(set ^ 1, rst, rks, n + 2);
-        }
-        if constexpr (DMA) dma1(dsrc, dst, q0 + n);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-    constexpr std::true_type yes{};
-    constexpr std::false_type no{};
     {
       const Src s0 = src_of(0);
 #pragma unroll
@@ -442,59 +418,56 @@ __device__ __forceinline__ void gemm_tile(const ProbDev *probs, char *ws, const 
     if (nkt > 1) {
       const Src s1 = src_of(1);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) dma1(s1, 1, q);
+      for (int q = 0; q < 16; ++q) dma1(s1, 1, q);
     }
     read_frags(0, 0, 0);
-    // One stage of the loop; DMAB / DMAA say whether stage kt+1 (B rows)
-    // and stage kt+2 (A rows) exist.  The last two stages are peeled off
-    // with those loads compiled out: a runtime test inside the MFMA groups
-    // splits them into basic blocks and costs more than it saves, and
-    // issuing them anyway (clamped to the last stage) leaves the epilogue
-    // waiting for loads nobody reads.
-    auto body = [&](int kt, auto dmab, auto dmaa) {
+    // One stage: k-step 0 reads k-step 1 of this stage; the barrier (stage
+    // kt+1 landed, every wave is done reading stage kt); k-step 1 reads
+    // k-step 0 of stage kt+1 and loads stage kt+2 into the freed buffer, one
+    // DMA instruction per MFMA group.  The last two stages are peeled off
+    // with those loads compiled out.
+    auto body = [&](int kt, auto load) {
       const int st = kt & 1;
-      const Src nb = src_of(kt + 1), na = src_of(kt + 2);
-      kstep(0, yes, st, 1, dmab, nb, st ^ 1, 8);   // B rows of stage kt+1
-      kstep(1, yes, st, 2, no, nb, 0, 0);
-      kstep(0, yes, st, 3, no, nb, 0, 0);
-      // stage kt+1 landed and every wave is done reading stage kt
+      kstep(0, st, 1, no_dma);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      kstep(1, yes, st ^ 1, 0, dmaa, na, st, 0);   // A rows of stage kt+2
+      if constexpr (decltype(load)::value) {
+        const Src nn = src_of(kt + 2);
+        kstep(1, st ^ 1, 0, [&](int n) { dma1(nn, st, n); });
+      } else {
+        kstep(1, st ^ 1, 0, no_dma);
+      }
     };
+    constexpr std::true_type yes{};
+    constexpr std::false_type no{};
     int kt = 0;
-    for (; kt < nkt - 2; ++kt) body(kt, yes, yes);
-    if (kt == nkt - 2) { body(kt, yes, no); ++kt; }
-    body(kt, no, no);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    for (; kt < nkt - 2; ++kt) body(kt, yes);
+    if (kt == nkt - 2) { body(kt, no); ++kt; }
+    body(kt, no);
   } else {
-  stage(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (nkt > 1) stage(1, 1);
-  read_frags(0, 0, 0);
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int st = kt & 1;
-    // k-steps 0..2: MFMAs of step s, reads of step s+1 (same stage)
-    read_frags(1, st, 1);
-    mfmas(0);
-    interleave();
-    read_frags(0, st, 2);
-    mfmas(1);
-    interleave();
-    read_frags(1, st, 3);
-    mfmas(0);
-    interleave();
-    // stage t+1 landed and every wave is done reading stage t: sync, then
-    // refill buffer st with stage t+2 and start reading stage t+1
+    // K not a multiple of 64: the same pipeline, stages loaded by stage()
+    stage(0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (kt + 2 < nkt) stage(kt + 2, st);
-    if (kt + 1 < nkt) read_frags(0, st ^ 1, 0);
-    mfmas(1);
-    interleave();
+    if (nkt > 1) stage(1, 1);
+    read_frags(0, 0, 0);
+    for (int kt = 0; kt < nkt; ++kt) {
+      const int st = kt & 1;
+      kstep(0, st, 1, no_dma);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (kt + 2 < nkt) stage(kt + 2, st);
+      kstep(1, st ^ 1, 0, no_dma);
+    }
   }
-  }
+
+  // the last MFMAs' results are complete before anything reads them: the
+  // in-place form hides their latency from the compiler
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
 
   // ---- epilogue: C = s^p (cd D + cacc acc) + cdiag I, stored to S0/S1.
   // The tile leaves registers in four passes of 64 rows (block row p of
@@ -543,11 +516,12 @@ __device__ __forceinline__ void gemm_tile(const ProbDev *probs, char *ws, const 
   // 64 distinct banks, and the two half-waves of an accumulator write still
   // land 32 banks apart.
   auto srow = [](int r) { return (r & ~7) | ((r + ((r >> 3) & 3) * 2) & 7); };
-  auto put = [&](const f32x16_t &blk, int j) {
+  // block (i, j) of 16 x 16: lane L holds rows 4 (L/16) .. +4, column L%16
+  auto put = [&](const f32x4_t &blk, int ih, int j) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int r = wm * 32 + 8 * (v >> 2) + 4 * lg + (v & 3);
-      stg[srow(r) * SLD + wn * 128 + j * 32 + lr] = blk[v] * R.cacc;
+    for (int v = 0; v < 4; ++v) {
+      const int r = wm * 32 + ih * 16 + 4 * lg + v;
+      stg[srow(r) * SLD + wn * 128 + j * 16 + lr] = blk[v] * R.cacc;
     }
   };
 #pragma unroll 1
@@ -568,10 +542,15 @@ __device__ __forceinline__ void gemm_tile(const ProbDev *probs, char *ws, const 
         if (dsplit) dq2[q] = *reinterpret_cast<const uint4 *>(D2 + e * 2);
       }
     }
-    if (p == 0) { put(acc[0][0], 0); put(acc[0][1], 1); put(acc[0][2], 2); put(acc[0][3], 3); }
-    if (p == 1) { put(acc[1][0], 0); put(acc[1][1], 1); put(acc[1][2], 2); put(acc[1][3], 3); }
-    if (p == 2) { put(acc[2][0], 0); put(acc[2][1], 1); put(acc[2][2], 2); put(acc[2][3], 3); }
-    if (p == 3) { put(acc[3][0], 0); put(acc[3][1], 1); put(acc[3][2], 2); put(acc[3][3], 3); }
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      if (p == pp) {
+#pragma unroll
+        for (int ih = 0; ih < 2; ++ih)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) put(acc[2 * pp + ih][j], ih, j);
+      }
+    }
     __syncthreads();
     // fast row phase; HAS_D: D chunks in dq (and dq2 when split)
     auto row_fast = [&](auto has_d) {
