@@ -225,7 +225,7 @@ struct Src {
 // SPLIT: the recipe may carry K segments, a split D and a split output; the
 // plain instance keeps the single-segment pipeline free of them.
 // LDS of both kernels: two stage buffers of both operands (the epilogue
-// stages through the first 67.5 KB), then a slot through which the
+// stages through the first 66 KB), then a slot through which the
 // persistent kernel hands a work item to every wave.
 constexpr int LDS_SLOT = 2 * 2 * OPB;
 __shared__ __attribute__((aligned(1024))) char lds[LDS_SLOT + 64];
