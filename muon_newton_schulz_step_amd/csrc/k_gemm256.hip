@@ -535,6 +535,11 @@ __device__ __forceinline__ void gemm_tile(const ProbDev *probs, char *ws, const 
   char *S1 = R.rS1 >= 0 ? ws + P.off[R.rS1] : nullptr;
   const int64_t ld1 = R.rS1 >= 0 ? P.ld[R.rS1] : 0;
   const bool col_phase = t0 || (S1 && t1) || mirror;
+  // the scale is folded into the staged accumulators, so staged values are
+  // final unless D or the diagonal change them: only then does the row
+  // phase write its values back for the column phase
+  const float cs = R.cacc * sc, cds = R.cd * sc;
+  const bool wback = col_phase && (D != nullptr || diag);
   // Interior tile with bf16 operands and 16-byte aligned rows: the row phase
   // takes 8-column chunks with the D chunks of a pass loaded up front, so no
   // wait on the vector-memory counter (which also counts stores) falls
@@ -553,7 +558,7 @@ __device__ __forceinline__ void gemm_tile(const ProbDev *probs, char *ws, const 
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int r = wm * 32 + ih * 16 + 4 * lg + v;
-      stg[srow(r) * SLD + wn * 128 + j * 16 + lr] = blk[v] * R.cacc;
+      stg[srow(r) * SLD + wn * 128 + j * 16 + lr] = blk[v] * cs;
     }
   };
 #pragma unroll 1
@@ -607,10 +612,8 @@ __device__ __forceinline__ void gemm_tile(const ProbDev *probs, char *ws, const 
             for (int e = 0; e < 8; ++e) dv[e] += dl[e];
           }
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = fmaf(R.cd, dv[e], v[e]);
+          for (int e = 0; e < 8; ++e) v[e] = fmaf(cds, dv[e], v[e]);
         }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] *= sc;
         if (diag) {
           const int64_t dd = gi - gj;
           if (dd >= 0 && dd < 8) {
@@ -619,7 +622,7 @@ __device__ __forceinline__ void gemm_tile(const ProbDev *probs, char *ws, const 
               if (e == dd) v[e] += R.cdiag;
           }
         }
-        if (col_phase) {
+        if (wback) {
           *reinterpret_cast<float4 *>(src) = make_float4(v[0], v[1], v[2], v[3]);
           *reinterpret_cast<float4 *>(src + 4) = make_float4(v[4], v[5], v[6], v[7]);
         }
@@ -669,12 +672,11 @@ __device__ __forceinline__ void gemm_tile(const ProbDev *probs, char *ws, const 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float x = v[e];
-          if (D) x = fmaf(R.cd, dv[e], x);
-          x *= sc;
+          if (D) x = fmaf(cds, dv[e], x);
           if (diag && gi == gj + e) x += R.cdiag;
           v[e] = x;
         }
-        if (col_phase) *reinterpret_cast<float4 *>(src) = make_float4(v[0], v[1], v[2], v[3]);
+        if (wback) *reinterpret_cast<float4 *>(src) = make_float4(v[0], v[1], v[2], v[3]);
         if (nv > 0) {
           if (osplit) {
             float hi[4], lo[4];
