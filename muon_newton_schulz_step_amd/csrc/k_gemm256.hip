@@ -75,12 +75,18 @@ __device__ __forceinline__ int swz(int r, int c) {
 #endif
 }
 
-// c += a b on v_mfma_f32_16x16x32_bf16 with the accumulator tied in place
-// (the compiler's own selection of this instruction picks a destination
-// apart from the accumulator and rotates 64 blocks every loop trip).
-// Results are read only after mfma_drain().
+// c += a b on v_mfma_f32_16x16x32_bf16.  In the main loop the accumulator
+// is tied in place through inline asm (the compiler's own selection of the
+// instruction picks a destination apart from the accumulator and rotates 64
+// blocks through copies every loop trip); the compiler does not see the
+// latency of those, so every accumulator's last product (the tile's final
+// k-step, LAST) goes through the builtin, whose result latency the compiler
+// covers before anything reads it.  An asm product is then read only by the
+// MFMAs of the next k-step, 64 instructions later.
+template <bool LAST = false>
 __device__ __forceinline__ void mfma16(f32x4_t &c, const bf16x8_t &a, const bf16x8_t &b) {
-  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  if constexpr (LAST) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  else asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
@@ -369,12 +375,12 @@ __device__ __forceinline__ void gemm_tile(const ProbDev *probs, char *ws, const 
   // fragment reads of the next step (stage buffer rst, k-step rks) in
   // groups 0..11, two in each of groups 0..3, so they land four groups
   // before the next step needs them.  sched_barrier keeps this order.
-  auto kstep = [&](int set, int rst, int rks) {
+  auto kstep = [&](int set, int rst, int rks, auto last) {
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
       const int i = n >> 1, j = (n & 1) * 4;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) mfma16(acc[i][j + jj], fa[set][i], fb[set][j + jj]);
+      for (int jj = 0; jj < 4; ++jj) mfma16<decltype(last)::value>(acc[i][j + jj], fa[set][i], fb[set][j + jj]);
       __builtin_amdgcn_sched_barrier(0);
       if (n < 4) { read1(set ^ 1, rst, rks, 2 * n); read1(set ^ 1, rst, rks, 2 * n + 1); }
       else if (n < 12) read1(set ^ 1, rst, rks, n + 4);
@@ -435,8 +441,9 @@ __device__ __forceinline__ void gemm_tile(const ProbDev *probs, char *ws, const 
     constexpr int kDma0 = 15 - kBar1;       // DMA instructions in k-step 0
     constexpr int kDma1 = 16 - kDma0;       // in k-step 1
     static_assert(kDma0 == 6, "the vmcnt immediate of barrier 2");
-    auto body = [&](int kt, auto load) {
+    auto body = [&](int kt, auto load, auto last) {
       constexpr bool LOAD = decltype(load)::value;
+      constexpr bool LAST = decltype(last)::value;
       const int st = kt & 1;
       const Src nn = src_of(LOAD ? kt + 2 : kt);
 #pragma unroll
@@ -458,7 +465,7 @@ __device__ __forceinline__ void gemm_tile(const ProbDev *probs, char *ws, const 
       for (int n = 0; n < 16; ++n) {
         const int i = n >> 1, j = (n & 1) * 4;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) mfma16(acc[i][j + jj], fa[1][i], fb[1][j + jj]);
+        for (int jj = 0; jj < 4; ++jj) mfma16<LAST>(acc[i][j + jj], fa[1][i], fb[1][j + jj]);
         __builtin_amdgcn_sched_barrier(0);
         if (n < 4) { read1(0, st ^ 1, 0, 2 * n); read1(0, st ^ 1, 0, 2 * n + 1); }
         else if (n < 12) read1(0, st ^ 1, 0, n + 4);
@@ -473,9 +480,9 @@ __device__ __forceinline__ void gemm_tile(const ProbDev *probs, char *ws, const 
     constexpr std::true_type yes{};
     constexpr std::false_type no{};
     int kt = 0;
-    for (; kt < nkt - 2; ++kt) body(kt, yes);
-    if (kt == nkt - 2) { body(kt, no); ++kt; }
-    body(kt, no);
+    for (; kt < nkt - 2; ++kt) body(kt, yes, no);
+    if (kt == nkt - 2) { body(kt, no, no); ++kt; }
+    body(kt, no, yes);
   } else {
     // K not a multiple of 64: the same pipeline, stages loaded by stage()
     stage(0, 0);
@@ -483,23 +490,19 @@ __device__ __forceinline__ void gemm_tile(const ProbDev *probs, char *ws, const 
     __syncthreads();
     if (nkt > 1) stage(1, 1);
     read_frags(0, 0, 0);
-    for (int kt = 0; kt < nkt; ++kt) {
+    constexpr std::true_type yes{};
+    constexpr std::false_type no{};
+    auto rstage = [&](int kt, auto last) {
       const int st = kt & 1;
-      kstep(0, st, 1);
+      kstep(0, st, 1, no);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (kt + 2 < nkt) stage(kt + 2, st);
-      kstep(1, st ^ 1, 0);
-    }
+      kstep(1, st ^ 1, 0, last);
+    };
+    for (int kt = 0; kt < nkt - 1; ++kt) rstage(kt, no);
+    rstage(nkt - 1, yes);
   }
-
-  // the last MFMAs' results are complete before anything reads them: the
-  // in-place form hides their latency from the compiler
-  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
 
   // ---- epilogue: C = s^p (cd D + cacc acc) + cdiag I, stored to S0/S1.
   // The tile leaves registers in four passes of 64 rows (block row p of
