@@ -3,7 +3,7 @@ whose result latency the compiler does not see.  Compile the kernel to gfx950
 assembly (CPU only, no device) and check that nothing reads an accumulator
 written by one of those MFMAs before the result can have landed: every
 non-MFMA read, and every MFMA reading it as an A or B operand, must follow
-the write by at least MIN_WAIT wait states along the fall-through code.  The
+the write by at least MIN_WAIT wait states on every path, branches included.  The
 checker itself is pinned on small listings with a planted early read."""
 
 from __future__ import annotations
@@ -38,59 +38,88 @@ def _agprs(tok: str) -> set[int]:
 
 def early_reads(listing: str) -> list[str]:
     """Reads of AGPRs written by an inline-asm MFMA fewer than MIN_WAIT wait
-    states earlier, scanning each function's code in layout order and
-    dropping the state at labels that only a branch reaches."""
-    bad: list[str] = []
-    pending: dict[int, int] = {}  # agpr -> wait-state clock at the asm MFMA write
-    clock = 0
-    in_asm = False
-    prev = ""
+    states earlier, along every path: the state is carried through
+    fall-through and into every branch target (the largest wait still owed
+    wins where paths meet), and each function is swept until the states at
+    its labels settle, so loop back-edges are covered too."""
+    funcs: list[list[str]] = []
     for raw in listing.splitlines():
         s = raw.strip()
         if re.match(r"^_Z\w+:", s):
-            pending, clock, prev = {}, 0, ""
+            funcs.append([])
             continue
-        if s.startswith(";;#ASMSTART"):
-            in_asm = True
-            continue
-        if s.startswith(";;#ASMEND"):
+        if funcs:
+            funcs[-1].append(s)
+    bad: set[str] = set()
+    for body in funcs:
+        at_label: dict[str, dict[int, int]] = {}
+        for _ in range(8):
+            changed = False
+            owed: dict[int, int] | None = {}  # agpr -> wait states still owed; None = unreachable
             in_asm = False
-            continue
-        if re.match(r"^\.LBB\w+:", s):
-            if prev in ("s_branch", "s_endpgm", "s_setpc_b64"):
-                pending = {}
-            continue
-        if not s or s.startswith(";") or s.startswith("."):
-            continue
-        op = s.split()[0]
-        prev = op
-        args = [a for a in re.split(r"[ ,]+", s[len(op):].strip()) if a]
-        if op.startswith("v_mfma"):
-            for a in args[1:3]:
-                for r in _agprs(a):
-                    if r in pending and clock - pending[r] < MIN_WAIT:
-                        bad.append(s)
-            clock += MFMA_WAIT
-            dst = _agprs(args[0]) if args else set()
-            for r in dst:
-                if in_asm:
-                    pending[r] = clock
-                else:
-                    pending.pop(r, None)
-            continue
-        if op == "s_nop":
-            clock += int(args[0], 0) + 1
-            continue
-        clock += 1
-        reads = args if op.startswith(_STORES) else args[1:]
-        for a in reads:
-            for r in _agprs(a):
-                if r in pending and clock - pending[r] < MIN_WAIT:
-                    bad.append(s)
-        if args and not op.startswith(_STORES) and not op.startswith("s_"):
-            for r in _agprs(args[0]):
-                pending.pop(r, None)
-    return bad
+
+            def spend(n: int) -> None:
+                for r in list(owed):
+                    owed[r] -= n
+                    if owed[r] <= 0:
+                        del owed[r]
+
+            def send(target: str) -> None:
+                nonlocal changed
+                cur = at_label.setdefault(target, {})
+                for r, w in owed.items():
+                    if cur.get(r, 0) < w:
+                        cur[r] = w
+                        changed = True
+
+            for s in body:
+                if s.startswith(";;#ASMSTART"):
+                    in_asm = True
+                    continue
+                if s.startswith(";;#ASMEND"):
+                    in_asm = False
+                    continue
+                m = re.match(r"^(\.LBB\w+):", s)
+                if m:
+                    merged = dict(at_label.get(m.group(1), {}))
+                    for r, w in (owed or {}).items():
+                        merged[r] = max(merged.get(r, 0), w)
+                    owed = merged
+                    continue
+                if not s or s.startswith(";") or s.startswith(".") or owed is None:
+                    continue
+                op = s.split()[0]
+                args = [a for a in re.split(r"[ ,]+", s[len(op):].strip()) if a]
+                if op.startswith("s_branch") or op.startswith("s_cbranch"):
+                    send(args[0])
+                    if op.startswith("s_branch"):
+                        owed = None
+                    continue
+                if op in ("s_endpgm", "s_setpc_b64"):
+                    owed = None
+                    continue
+                if op.startswith("v_mfma"):
+                    for a in args[1:3]:
+                        if any(r in owed for r in _agprs(a)):
+                            bad.add(s)
+                    spend(MFMA_WAIT)
+                    for r in (_agprs(args[0]) if args else set()):
+                        if in_asm:
+                            owed[r] = MIN_WAIT
+                        else:
+                            owed.pop(r, None)
+                    continue
+                spend(int(args[0], 0) + 1 if op == "s_nop" else 1)
+                reads = args if op.startswith(_STORES) else args[1:]
+                for a in reads:
+                    if any(r in owed for r in _agprs(a)):
+                        bad.add(s)
+                if args and not op.startswith(_STORES) and not op.startswith("s_"):
+                    for r in _agprs(args[0]):
+                        owed.pop(r, None)
+            if not changed:
+                break
+    return sorted(bad)
 
 
 def test_checker_catches_a_planted_early_read():
@@ -117,10 +146,30 @@ def test_checker_catches_a_planted_early_read():
         ".LBB0_1:",
         "v_accvgpr_read_b32 v8, a0",
     ])
+    via_branch = "\n".join([
+        "_Zk:",
+        ";;#ASMSTART", "v_mfma_f32_16x16x32_bf16 a[0:3], v[0:3], v[4:7], a[0:3]", ";;#ASMEND",
+        "s_cbranch_scc1 .LBB0_2",
+        "s_nop 15", "s_nop 7",
+        "s_endpgm",
+        ".LBB0_2:",
+        "v_accvgpr_read_b32 v8, a1",
+    ])
+    back_edge = "\n".join([
+        "_Zk:",
+        ".LBB0_1:",
+        "v_accvgpr_read_b32 v8, a2",
+        "s_nop 15", "s_nop 7",
+        ";;#ASMSTART", "v_mfma_f32_16x16x32_bf16 a[0:3], v[0:3], v[4:7], a[0:3]", ";;#ASMEND",
+        "s_cbranch_scc1 .LBB0_1",
+        "s_endpgm",
+    ])
     assert early_reads(ok) == []
     assert early_reads(early) == ["v_accvgpr_mov_b32 a9, a2"]
     assert early_reads(builtin) == []       # the compiler covers its own MFMAs
-    assert early_reads(branch_only) == []   # not reached by fall-through
+    assert early_reads(branch_only) == []   # the read is on no path from the MFMA
+    assert early_reads(via_branch) == ["v_accvgpr_read_b32 v8, a1"]
+    assert early_reads(back_edge) == ["v_accvgpr_read_b32 v8, a2"]
 
 
 def test_large_tile_gemm_reads_no_asm_mfma_result_early(tmp_path):
