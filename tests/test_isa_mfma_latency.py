@@ -23,8 +23,21 @@ CSRC = os.path.join(ROOT, "muon_newton_schulz_step_amd", "csrc")
 # (the fewest cycles between two MFMA issues).
 MIN_WAIT = 18
 MFMA_WAIT = 4
+# A VALU write of a VGPR or AGPR needs 2 wait states before an MFMA reads it;
+# the compiler inserts them for its own MFMAs only.  Checked with margin.
+VALU_WAIT = 3
 
 _STORES = ("ds_write", "global_store", "buffer_store", "scratch_store", "flat_store")
+
+
+def _regs(tok: str) -> set[str]:
+    """Registers a VGPR or AGPR operand names, as 'v12' / 'a12'."""
+    tok = tok.strip()
+    m = re.match(r"([av])\[(\d+):(\d+)\]$", tok)
+    if m:
+        return {m.group(1) + str(i) for i in range(int(m.group(2)), int(m.group(3)) + 1)}
+    m = re.match(r"([av])(\d+)$", tok)
+    return {tok} if m else set()
 
 
 def _agprs(tok: str) -> set[int]:
@@ -37,8 +50,11 @@ def _agprs(tok: str) -> set[int]:
 
 
 def early_reads(listing: str) -> list[str]:
-    """Reads of AGPRs written by an inline-asm MFMA fewer than MIN_WAIT wait
-    states earlier, along every path: the state is carried through
+    """Two hazards the compiler cannot see through inline asm, along every
+    path: a read of an AGPR written by an inline-asm MFMA fewer than MIN_WAIT
+    wait states earlier, and an inline-asm MFMA reading (as A, B or C) a
+    register that a VALU instruction (v_accvgpr_write / mov included) wrote
+    fewer than VALU_WAIT wait states earlier.  The state is carried through
     fall-through and into every branch target (the largest wait still owed
     wins where paths meet), and each function is swept until the states at
     its labels settle, so loop back-edges are covered too."""
@@ -52,24 +68,26 @@ def early_reads(listing: str) -> list[str]:
             funcs[-1].append(s)
     bad: set[str] = set()
     for body in funcs:
-        at_label: dict[str, dict[int, int]] = {}
+        # owed: ("m", agpr) -> wait states an asm MFMA result still needs;
+        #       ("w", reg)  -> wait states a VALU write still needs before an asm MFMA reads it
+        at_label: dict[str, dict[tuple, int]] = {}
         for _ in range(8):
             changed = False
-            owed: dict[int, int] | None = {}  # agpr -> wait states still owed; None = unreachable
+            owed: dict[tuple, int] | None = {}  # None = unreachable
             in_asm = False
 
-            def spend(n: int) -> None:
-                for r in list(owed):
-                    owed[r] -= n
-                    if owed[r] <= 0:
-                        del owed[r]
+            def spend(n_mfma: int, n_valu: int) -> None:
+                for key in list(owed):
+                    owed[key] -= n_mfma if key[0] == "m" else n_valu
+                    if owed[key] <= 0:
+                        del owed[key]
 
             def send(target: str) -> None:
                 nonlocal changed
                 cur = at_label.setdefault(target, {})
-                for r, w in owed.items():
-                    if cur.get(r, 0) < w:
-                        cur[r] = w
+                for key, w in owed.items():
+                    if cur.get(key, 0) < w:
+                        cur[key] = w
                         changed = True
 
             for s in body:
@@ -82,8 +100,8 @@ def early_reads(listing: str) -> list[str]:
                 m = re.match(r"^(\.LBB\w+):", s)
                 if m:
                     merged = dict(at_label.get(m.group(1), {}))
-                    for r, w in (owed or {}).items():
-                        merged[r] = max(merged.get(r, 0), w)
+                    for key, w in (owed or {}).items():
+                        merged[key] = max(merged.get(key, 0), w)
                     owed = merged
                     continue
                 if not s or s.startswith(";") or s.startswith(".") or owed is None:
@@ -100,23 +118,29 @@ def early_reads(listing: str) -> list[str]:
                     continue
                 if op.startswith("v_mfma"):
                     for a in args[1:3]:
-                        if any(r in owed for r in _agprs(a)):
+                        if any(("m", r) in owed for r in _agprs(a)):
                             bad.add(s)
-                    spend(MFMA_WAIT)
+                    if in_asm and any(("w", r) in owed for a in args[1:4] for r in _regs(a)):
+                        bad.add(s)
+                    spend(MFMA_WAIT, 1)
                     for r in (_agprs(args[0]) if args else set()):
                         if in_asm:
-                            owed[r] = MIN_WAIT
+                            owed[("m", r)] = MIN_WAIT
                         else:
-                            owed.pop(r, None)
+                            owed.pop(("m", r), None)
                     continue
-                spend(int(args[0], 0) + 1 if op == "s_nop" else 1)
+                n = int(args[0], 0) + 1 if op == "s_nop" else 1
+                spend(n, n)
                 reads = args if op.startswith(_STORES) else args[1:]
                 for a in reads:
-                    if any(r in owed for r in _agprs(a)):
+                    if any(("m", r) in owed for r in _agprs(a)):
                         bad.add(s)
                 if args and not op.startswith(_STORES) and not op.startswith("s_"):
                     for r in _agprs(args[0]):
-                        owed.pop(r, None)
+                        owed.pop(("m", r), None)
+                    if op.startswith("v_"):
+                        for r in _regs(args[0]):
+                            owed[("w", r)] = VALU_WAIT
             if not changed:
                 break
     return sorted(bad)
@@ -164,6 +188,25 @@ def test_checker_catches_a_planted_early_read():
         "s_cbranch_scc1 .LBB0_1",
         "s_endpgm",
     ])
+    valu_then_asm = "\n".join([
+        "_Zk:",
+        "v_accvgpr_write_b32 a3, v9",
+        ";;#ASMSTART", "v_mfma_f32_16x16x32_bf16 a[0:3], v[0:3], v[4:7], a[0:3]", ";;#ASMEND",
+    ])
+    valu_spaced = "\n".join([
+        "_Zk:",
+        "v_mov_b32 v5, v9",
+        "s_nop 2",
+        ";;#ASMSTART", "v_mfma_f32_16x16x32_bf16 a[0:3], v[0:3], v[4:7], a[0:3]", ";;#ASMEND",
+    ])
+    valu_then_builtin = "\n".join([
+        "_Zk:",
+        "v_accvgpr_write_b32 a3, v9",
+        "v_mfma_f32_16x16x32_bf16 a[0:3], v[0:3], v[4:7], a[0:3]",
+    ])
+    assert early_reads(valu_then_asm) == ["v_mfma_f32_16x16x32_bf16 a[0:3], v[0:3], v[4:7], a[0:3]"]
+    assert early_reads(valu_spaced) == []
+    assert early_reads(valu_then_builtin) == []   # the compiler covers its own MFMAs
     assert early_reads(ok) == []
     assert early_reads(early) == ["v_accvgpr_mov_b32 a9, a2"]
     assert early_reads(builtin) == []       # the compiler covers its own MFMAs
