@@ -8,6 +8,7 @@ checker itself is pinned on small listings with a planted early read."""
 
 from __future__ import annotations
 
+import importlib.util
 import os
 import re
 import shutil
@@ -220,9 +221,11 @@ def test_large_tile_gemm_reads_no_asm_mfma_result_early(tmp_path):
     if hipcc is None:
         pytest.skip("hipcc is not available")
     out = str(tmp_path / "k_gemm256.s")
-    cmd = [hipcc, "-O3", "-std=c++17", "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", CSRC, "--cuda-device-only", "-S",
-           os.path.join(CSRC, "k_gemm256.hip"), "-o", out]
+    # the library's own compile flags, so the listing is the code it ships
+    spec = importlib.util.spec_from_file_location("_muon_build", os.path.join(ROOT, "muon_newton_schulz_step_amd", "build.py"))
+    build = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(build)
+    cmd = [hipcc, *build.COMMON, "--cuda-device-only", "-S", os.path.join(CSRC, "k_gemm256.hip"), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stderr[-4000:]
     listing = open(out).read()
